@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the decode indexer path on one MI355X.
+
+One step = one pass of the decode hot path over one batch:
+  indexer_score_decode  (fused NVFP4 dequant + per-page scores, 4 requests x 8
+                         query slots x 4 heads, 500,000-token contexts: 3,906
+                         pages of 9,216 bytes per request)
+  topk16_select         (the 128 score rows: 15 best pages below the own page,
+                         then the own page)
+Inputs are resident in HBM before timing starts.  The index-K cache rotates
+over several independent pools (different layers in a real model) so that
+their total exceeds the 256 MB last-level cache and every step streams from
+HBM.
+
+Prints one JSON line.  `value` is index-K bytes scored per second over the
+whole step (GB/s); `roofline` reports the score kernel's own average launch
+duration against the HBM peak; `cpu_baseline` is the CPU oracle timed on a
+bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--pools P]
+  python bench.py --profile-pass     # short fixed sequence for rocprofv3 counter runs
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "index-K GB/s scored (frac of HBM peak) + top-16 rows/s, 500K-token decode"
+HBM_PEAK_GBS = 8000.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "score_decode_long_counters.txt")
+SCORE_SOURCES = ["score_decode.hip", "device_common.hpp", "nvfp4_lut.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in SCORE_SOURCES:
+        with open(os.path.join(ROOT, "page_scoring_top_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_counters():
+    """HBM traffic per launch of the score kernel from the committed rocprofv3
+    counter summary, or None when it is missing or the kernel changed since."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    kv = {}
+    for line in open(COUNTERS_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--pools", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the indexer path "
+                          "has no multi-GPU mode", "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import page_scoring_top_amd as ps
+    import workloads
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    d = workloads.long_decode()
+    R, W, qlen = d.num_reqs, d.width, d.qlen
+    P = max(1, args.pools)
+
+    # Index-K pools: pool 0 is the seeded host workload; the others are drawn
+    # on the device with their own seeded generator (same distributions:
+    # uniform code bytes, scale bytes uniform over 0x01..0x7E).
+    pools = [torch.from_numpy(d.kv_cache).to(dev)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    for _ in range(1, P):
+        kv = torch.empty_like(pools[0])
+        kv[:, :8192] = torch.randint(0, 256, (kv.shape[0], 8192), generator=gen, device=dev,
+                                     dtype=torch.uint8)
+        kv[:, 8192:] = torch.randint(1, 127, (kv.shape[0], 1024), generator=gen, device=dev,
+                                     dtype=torch.uint8)
+        pools.append(kv)
+    bt = torch.from_numpy(d.block_table).to(dev)
+    seq = torch.from_numpy(d.seq_lens).to(dev)
+    q = torch.from_numpy(d.q).to(dev)
+    qs = torch.from_numpy(d.q_scale).to(dev)
+    scores = torch.zeros((R, 32, W), dtype=torch.float32, device=dev)
+    own = torch.zeros((R, 32), dtype=torch.int32, device=dev)
+    out = torch.zeros((R * 32, 16), dtype=torch.int32, device=dev)
+
+    score_calls = [ps.prepare(ps.indexer_score_decode, kv, bt, seq, q, qs, qlen, W, scores, own)
+                   for kv in pools]
+    topk_call = ps.prepare(ps.topk16_select, scores.view(R * 32, W), W, out,
+                           valid_len=own.view(-1), append_page=own.view(-1))
+
+    pages = sum(min(max((int(s) - 1) // 128, 0), W) for s in d.seq_lens[:R])
+    kbytes = pages * 9216
+    stored = 32 * pages  # each of a request's 32 rows stores each of its scored pages
+    # Algorithmic bytes of one score launch: index-K pages, their block-table
+    # entries, score writes, and per request q, q_scale, seq_len and own pages.
+    algo_bytes = pages * (9216 + 4) + stored * 4 + R * (4096 + 128 + 4 + 128)
+
+    if args.profile_pass:
+        # Fixed sequence for counter runs: a plain 1 GiB device copy (the
+        # calibration of FETCH_SIZE / WRITE_SIZE), then one score launch per pool.
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        for c in score_calls:
+            c()
+        topk_call()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_pass": True, "copy_bytes": 1 << 30, "score_launches": P,
+                          "score_algo_bytes": algo_bytes}), flush=True)
+        return
+
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        score_calls[i % P]()
+        topk_call()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        e0, e1, e2 = ev[i]
+        e0.record(stream)
+        score_calls[i % P]()
+        e1.record(stream)
+        topk_call()
+        e2.record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    score_ms = [e0.elapsed_time(e1) for e0, e1, _ in ev]
+    topk_ms = [e1.elapsed_time(e2) for _, e1, e2 in ev]
+    ms_per_step = total_ms / K
+    score_avg = float(np.mean(score_ms))
+    topk_avg = float(np.mean(topk_ms))
+
+    value = kbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = algo_bytes / (score_avg * 1e-3) / 1e9
+    traffic = read_counters()
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 products, f32 accumulate (NVFP4 keys)",
+        "data": "synthetic",
+        "config": {
+            "workload": "long-context decode: 4 requests x 8 query slots x 4 index heads, "
+                        "500,000-token contexts (3,906 NVFP4 pages scored per request), "
+                        "then top-16 of 128 score rows",
+            "requests": R, "query_slots": 8, "heads": 4, "depth": 128, "seq_len": 500000,
+            "pages_scored": pages, "index_k_bytes": kbytes, "width": W, "index_k_pools": P,
+            "parallelism": "single GPU",
+        },
+        "top16_rows_per_s": round(R * 32 / (topk_avg * 1e-3), 1),
+        "kernels_us": {"indexer_score_decode": round(score_avg * 1e3, 3),
+                       "topk16_select": round(topk_avg * 1e3, 3),
+                       "indexer_score_decode_min": round(min(score_ms) * 1e3, 3)},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "indexer_score_decode",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": algo_bytes,
+        },
+    }
+
+    if not args.no_cpu:
+        import oracle
+        # Oracle: all 32 rows of request 0 for as many pages as fit the time
+        # budget, extrapolated to the step's pages, plus its top-16 of the GPU's
+        # 128 score rows.
+        t0 = time.perf_counter()
+        n = 0
+        while n < pages and time.perf_counter() - t0 < args.cpu_seconds:
+            oracle.score_decode_column(d.kv_cache, d.block_table, d.seq_lens, d.q, d.q_scale,
+                                       qlen, W, 0, n)
+            n += 1
+        t_cols = time.perf_counter() - t0
+        s_host = scores.view(R * 32, W).cpu().numpy()
+        o_host = own.view(-1).cpu().numpy()
+        t1 = time.perf_counter()
+        oracle.topk16(s_host, o_host, None, None, o_host)
+        t_topk = time.perf_counter() - t1
+        cpu_step = t_cols * pages / n + t_topk
+        result["cpu_baseline"] = {
+            "value": round(kbytes / cpu_step / 1e9, 6),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"oracle decode scores of {n} pages x 32 rows of request 0 "
+                      f"({t_cols:.2f} s), scaled to {pages} pages, plus the oracle top-16 of "
+                      f"all 128 rows ({t_topk:.3f} s); step estimate {cpu_step:.1f} s",
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,134 @@
+// api.hip -- the exported C ABI (declared in include/pagescore.h): host-side
+// argument checks, then one stream-ordered launch per call.  Nothing here
+// synchronizes with the host or allocates memory.
+#include <hip/hip_runtime.h>
+#include <cstdint>
+#include <mutex>
+
+#include "launch.hpp"
+#include "pagescore.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int launch_status(hipError_t e)
+{
+    if (e == hipSuccess)
+        return PAGESCORE_OK;
+    g_last_hip_error = (int)e;
+    return PAGESCORE_ELAUNCH;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Compute units of the current device, queried once per device.
+int current_device_cus()
+{
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+bool page_args_ok(const uint8_t *kv, int64_t page_stride, int64_t num_blocks)
+{
+    return kv && aligned16(kv) && page_stride >= PAGESCORE_PAGE_BYTES && (page_stride % 16) == 0 &&
+           num_blocks >= 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_index_k_dequant(const uint8_t *kv_cache, int64_t page_stride_bytes, int64_t num_blocks,
+                          const int32_t *block_table, int64_t bt_stride, const int32_t *num_pages,
+                          const int32_t *page_offsets, int32_t num_reqs, int32_t max_num_pages,
+                          uint8_t *out, int64_t out_pages, void *stream)
+{
+    if (num_reqs < 0 || max_num_pages < 0)
+        return PAGESCORE_EINVAL;
+    if (num_reqs == 0 || max_num_pages == 0)
+        return PAGESCORE_OK;
+    if (!page_args_ok(kv_cache, page_stride_bytes, num_blocks) || !block_table || !num_pages ||
+        !page_offsets || !out || !aligned16(out) || out_pages < 0 || bt_stride < max_num_pages)
+        return PAGESCORE_EINVAL;
+    return launch_status(pagescore::launch_nvfp4_dequant(
+        kv_cache, page_stride_bytes, num_blocks, block_table, bt_stride, num_pages, page_offsets,
+        num_reqs, max_num_pages, out, out_pages, (hipStream_t)stream));
+}
+
+int indexer_score_decode(const uint8_t *kv_cache, int64_t page_stride_bytes, int64_t num_blocks,
+                         const int32_t *block_table, int64_t bt_stride, const int32_t *seq_lens,
+                         const uint8_t *q, const float *q_scale, int32_t num_reqs, int32_t qlen,
+                         int32_t width, float *scores, int32_t *row_own, void *stream)
+{
+    if (num_reqs < 0 || num_reqs > pagescore::kDecodeMaxReqs || qlen < 1 ||
+        qlen > PAGESCORE_SLOTS || width < 1)
+        return PAGESCORE_EINVAL;
+    if (num_reqs == 0)
+        return PAGESCORE_OK;
+    if (!page_args_ok(kv_cache, page_stride_bytes, num_blocks) || !block_table ||
+        bt_stride < width || !seq_lens || !q || !aligned16(q) || !q_scale || !scores)
+        return PAGESCORE_EINVAL;
+    return launch_status(pagescore::launch_score_decode(
+        kv_cache, page_stride_bytes, num_blocks, block_table, bt_stride, seq_lens, q, q_scale,
+        num_reqs, qlen, width, scores, row_own, current_device_cus(), (hipStream_t)stream));
+}
+
+int indexer_score_prefill(const uint8_t *q, const float *q_scale, const uint8_t *k,
+                          const float *k_scale, int32_t T, int32_t H, int32_t N, float *scores,
+                          int64_t ld, void *stream)
+{
+    if (T < 0 || N < 0 || H < 1 || H > pagescore::kPrefillMaxHeads)
+        return PAGESCORE_EINVAL;
+    if (T == 0 || N == 0)
+        return PAGESCORE_OK;
+    if (!q || !aligned16(q) || !q_scale || !k || !aligned16(k) || !k_scale || !scores || ld < N)
+        return PAGESCORE_EINVAL;
+    return launch_status(pagescore::launch_score_prefill(q, q_scale, k, k_scale, T, H, N, scores, ld,
+                                                         (hipStream_t)stream));
+}
+
+int topk16_select(const float *scores, int64_t row_stride, int32_t num_rows, int32_t width,
+                  const int32_t *valid_len, const int32_t *force_begin, const int32_t *force_end,
+                  const int32_t *append_page, int32_t *out, int64_t out_stride, void *stream)
+{
+    if (num_rows < 0 || width < 1)
+        return PAGESCORE_EINVAL;
+    if (num_rows == 0)
+        return PAGESCORE_OK;
+    if (!scores || row_stride < width || !out || out_stride < PAGESCORE_TOPK ||
+        (force_begin == nullptr) != (force_end == nullptr))
+        return PAGESCORE_EINVAL;
+    return launch_status(pagescore::launch_topk16(scores, row_stride, num_rows, width, valid_len,
+                                                   force_begin, force_end, append_page, out,
+                                                   out_stride, (hipStream_t)stream));
+}
+
+int pagescore_last_hip_error(void) { return g_last_hip_error; }
+
+const char *pagescore_strerror(int code)
+{
+    switch (code) {
+    case PAGESCORE_OK:
+        return "ok";
+    case PAGESCORE_EINVAL:
+        return "invalid argument (host-side check)";
+    case PAGESCORE_ELAUNCH:
+        return "kernel launch failed (see pagescore_last_hip_error)";
+    default:
+        return "unknown error code";
+    }
+}
+
+}  // extern "C"

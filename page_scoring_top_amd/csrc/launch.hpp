@@ -1,0 +1,39 @@
+// launch.hpp -- internal launchers behind the C ABI (not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace pagescore {
+
+// Requests per indexer_score_decode call: the kernel keeps a per-request page
+// prefix sum in LDS (4 bytes per request).
+constexpr int32_t kDecodeMaxReqs = 8192;
+
+// Heads per indexer_score_prefill call: a work-group keeps one token's query
+// rows (heads rounded up to 32) as f16 in LDS.
+constexpr int32_t kPrefillMaxHeads = 224;
+
+hipError_t launch_nvfp4_dequant(const uint8_t *kv, int64_t page_stride, int64_t num_blocks,
+                                const int32_t *block_table, int64_t bt_stride,
+                                const int32_t *num_pages, const int32_t *page_offsets,
+                                int32_t num_reqs, int32_t max_num_pages, uint8_t *out,
+                                int64_t out_pages, hipStream_t stream);
+
+hipError_t launch_score_decode(const uint8_t *kv, int64_t page_stride, int64_t num_blocks,
+                               const int32_t *block_table, int64_t bt_stride,
+                               const int32_t *seq_lens, const uint8_t *q, const float *q_scale,
+                               int32_t num_reqs, int32_t qlen, int32_t width, float *scores,
+                               int32_t *row_own, int num_cus, hipStream_t stream);
+
+hipError_t launch_score_prefill(const uint8_t *q, const float *q_scale, const uint8_t *k,
+                                const float *k_scale, int32_t T, int32_t H, int32_t N,
+                                float *scores, int64_t ld, hipStream_t stream);
+
+hipError_t launch_topk16(const float *scores, int64_t row_stride, int32_t num_rows, int32_t width,
+                         const int32_t *valid_len, const int32_t *force_begin,
+                         const int32_t *force_end, const int32_t *append_page, int32_t *out,
+                         int64_t out_stride, hipStream_t stream);
+
+
+}  // namespace pagescore

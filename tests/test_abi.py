@@ -1,0 +1,150 @@
+"""The C ABI: libpagescore.so loads, exports every function include/pagescore.h
+declares, and its host-side argument checks reject bad calls before anything
+is enqueued (no GPU is touched on these paths, so they run on the CPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagescore.h")
+LIB = os.path.join(ROOT, "page_scoring_top_amd", "libpagescore.so")
+
+EINVAL = -22
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libpagescore.so is not built (python -m page_scoring_top_amd.build)")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_four_calls():
+    fns = declared_functions()
+    for name in ("nvfp4_index_k_dequant", "indexer_score_decode", "indexer_score_prefill",
+                 "topk16_select"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [f for f in declared_functions() if not hasattr(lib, f)]
+    assert not missing, missing
+
+
+def test_binding_loads_the_in_tree_library():
+    import page_scoring_top_amd as p
+    assert os.path.samefile(p.LIB_PATH, LIB)
+
+
+P = ctypes.c_void_p
+FAKE = P(0x1000)          # 16-byte aligned, never dereferenced on these paths
+ODD = P(0x1001)
+
+
+def _dequant(lib, **kw):
+    a = dict(kv=FAKE, stride=9216, nb=4, bt=FAKE, bts=8, num_pages=FAKE, offs=FAKE, R=2, maxp=8,
+             out=FAKE, out_pages=16)
+    a.update(kw)
+    f = lib.nvfp4_index_k_dequant
+    f.argtypes = [P, ctypes.c_int64, ctypes.c_int64, P, ctypes.c_int64, P, P, ctypes.c_int32,
+                  ctypes.c_int32, P, ctypes.c_int64, P]
+    return f(a["kv"], a["stride"], a["nb"], a["bt"], a["bts"], a["num_pages"], a["offs"], a["R"],
+             a["maxp"], a["out"], a["out_pages"], None)
+
+
+def test_dequant_host_checks(lib):
+    assert _dequant(lib, R=0) == 0                       # nothing to do: no launch
+    assert _dequant(lib, maxp=0) == 0
+    assert _dequant(lib, R=-1) == EINVAL
+    assert _dequant(lib, kv=None) == EINVAL
+    assert _dequant(lib, kv=ODD) == EINVAL               # misaligned
+    assert _dequant(lib, stride=9215) == EINVAL
+    assert _dequant(lib, stride=9224) == EINVAL          # not a multiple of 16
+    assert _dequant(lib, nb=0) == EINVAL
+    assert _dequant(lib, bts=7) == EINVAL                # narrower than max_num_pages
+    assert _dequant(lib, out=None) == EINVAL
+    assert _dequant(lib, out=ODD) == EINVAL
+    assert _dequant(lib, out_pages=-1) == EINVAL
+    assert _dequant(lib, num_pages=None) == EINVAL
+
+
+def _decode(lib, **kw):
+    a = dict(kv=FAKE, stride=9216, nb=4, bt=FAKE, bts=64, seq=FAKE, q=FAKE, qs=FAKE, R=1, qlen=1,
+             W=64, scores=FAKE, own=None)
+    a.update(kw)
+    f = lib.indexer_score_decode
+    f.argtypes = [P, ctypes.c_int64, ctypes.c_int64, P, ctypes.c_int64, P, P, P, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_int32, P, P, P]
+    return f(a["kv"], a["stride"], a["nb"], a["bt"], a["bts"], a["seq"], a["q"], a["qs"], a["R"],
+             a["qlen"], a["W"], a["scores"], a["own"], None)
+
+
+def test_decode_host_checks(lib):
+    assert _decode(lib, R=0) == 0
+    assert _decode(lib, R=-3) == EINVAL
+    assert _decode(lib, R=8193) == EINVAL                # beyond the per-call request limit
+    assert _decode(lib, qlen=0) == EINVAL
+    assert _decode(lib, qlen=9) == EINVAL
+    assert _decode(lib, W=0) == EINVAL
+    assert _decode(lib, bts=63) == EINVAL                # block table narrower than the width
+    assert _decode(lib, q=ODD) == EINVAL
+    assert _decode(lib, q=None) == EINVAL
+    assert _decode(lib, qs=None) == EINVAL
+    assert _decode(lib, scores=None) == EINVAL
+    assert _decode(lib, seq=None) == EINVAL
+    assert _decode(lib, kv=None) == EINVAL
+
+
+def _prefill(lib, **kw):
+    a = dict(q=FAKE, qs=FAKE, k=FAKE, ks=FAKE, T=4, H=2, N=8, scores=FAKE, ld=8)
+    a.update(kw)
+    f = lib.indexer_score_prefill
+    f.argtypes = [P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int64, P]
+    return f(a["q"], a["qs"], a["k"], a["ks"], a["T"], a["H"], a["N"], a["scores"], a["ld"], None)
+
+
+def test_prefill_host_checks(lib):
+    assert _prefill(lib, T=0) == 0
+    assert _prefill(lib, N=0) == 0
+    assert _prefill(lib, H=0) == EINVAL
+    assert _prefill(lib, H=225) == EINVAL               # beyond the LDS-resident head limit
+    assert _prefill(lib, T=-1) == EINVAL
+    assert _prefill(lib, ld=7) == EINVAL
+    assert _prefill(lib, q=ODD) == EINVAL
+    assert _prefill(lib, k=ODD) == EINVAL
+    assert _prefill(lib, ks=None) == EINVAL
+
+
+def _topk(lib, **kw):
+    a = dict(s=FAKE, rs=100, rows=3, W=100, valid=None, fb=None, fe=None, ap=None, out=FAKE, os=16)
+    a.update(kw)
+    f = lib.topk16_select
+    f.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, ctypes.c_int64, P]
+    return f(a["s"], a["rs"], a["rows"], a["W"], a["valid"], a["fb"], a["fe"], a["ap"], a["out"],
+             a["os"], None)
+
+
+def test_topk_host_checks(lib):
+    assert _topk(lib, rows=0) == 0
+    assert _topk(lib, rows=-1) == EINVAL
+    assert _topk(lib, W=0) == EINVAL
+    assert _topk(lib, rs=99) == EINVAL
+    assert _topk(lib, os=15) == EINVAL
+    assert _topk(lib, fb=FAKE) == EINVAL                 # begin without end
+    assert _topk(lib, out=None) == EINVAL
+    assert _topk(lib, s=None) == EINVAL
+
+
+def test_strerror(lib):
+    lib.pagescore_strerror.restype = ctypes.c_char_p
+    assert lib.pagescore_strerror(0) == b"ok"
+    assert b"invalid" in lib.pagescore_strerror(EINVAL)
