@@ -189,7 +189,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3 products, f32 accumulate (NVFP4 keys)",
+        "dtype": "e4m3 values as f16, f32 accumulate",
         "data": "synthetic",
         "config": {
             "workload": "long-context decode: 4 requests x 8 query slots x 4 index heads, "

@@ -118,8 +118,8 @@ int nvfp4_index_k_dequant(const uint8_t *kv_cache, int64_t page_stride_bytes,
  *                     its contents.
  *   row_own           nullable [num_reqs, 32] int32; receives every row's own
  *                     page, or -1 for rows without a query.
- * num_reqs == 0 returns PAGESCORE_OK with no launch; at most 8192 requests
- * per call (the kernel keeps a per-request prefix sum in LDS).
+ * num_reqs == 0 returns PAGESCORE_OK with no launch; at most 65535 requests
+ * per call (one grid row per request).
  */
 int indexer_score_decode(const uint8_t *kv_cache, int64_t page_stride_bytes,
                          int64_t num_blocks, const int32_t *block_table,

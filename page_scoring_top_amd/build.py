@@ -33,8 +33,11 @@ def hipcc() -> str:
 
 
 def common_flags():
+    # MFMA results in VGPRs: the epilogues read every accumulator, and the
+    # AGPR form would add one v_accvgpr_read per value.
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", INCLUDE, "-I", CSRC]
 
 

@@ -6,9 +6,8 @@
 
 namespace pagescore {
 
-// Requests per indexer_score_decode call: the kernel keeps a per-request page
-// prefix sum in LDS (4 bytes per request).
-constexpr int32_t kDecodeMaxReqs = 8192;
+// Requests per indexer_score_decode call: one grid row per request.
+constexpr int32_t kDecodeMaxReqs = 65535;
 
 // Heads per indexer_score_prefill call: a work-group keeps one token's query
 // rows (heads rounded up to 32) as f16 in LDS.

@@ -33,11 +33,20 @@
 //
 // Each output lane of a 16x16 tile holds 4 tokens of one query row, so the
 // page maximum is a running per-lane max over the 8 tiles, then 2 cross-lane
-// steps.  The kernel is persistent: the (request, page) pairs of the batch are
-// flattened and every wave takes one contiguous range, so ragged batches
-// balance; a wave prefetches the next page's 9 KiB while it scores the
-// current one.  Page ids come from a per-lane cache of the next 64
-// block-table entries.
+// steps.  On gfx950 the VALU and MFMA work of a SIMD largely serialize
+// (measured), so the per-page cost is their sum: the dequantization keeps to
+// 12 VALU operations per 8 elements on the common path, the MFMA results stay
+// in VGPRs, and pages whose scale bytes are all in 0x00..0x7E (no negative or
+// NaN scale) skip the sign-flip and NaN bookkeeping.
+//
+// Scheduling: work-group (x, b) covers request b; each of its waves owns a run
+// of `chunk` consecutive pages (chosen on the host from the batch size).  A
+// wave issues its first loads -- the request's length, the run's page ids and
+// the query rows -- all at once, so a single memory round trip precedes the
+// first page fetch; then it scores the run with two page buffers in turn, the
+// next page's 9 KiB in flight while the current one is scored.  Runs past a
+// request's last page exit at once, and the hardware dispatcher back-fills the
+// compute units, which balances ragged batches.
 //
 // NaN: the MFMA's NaN handling is not relied on.  A NaN scale byte makes every
 // dot of its token NaN, so it marks the whole page NaN; a NaN byte in a query
@@ -115,11 +124,9 @@ struct RequestRegs {
 };
 
 __device__ __forceinline__ void load_request(RequestRegs &rq, const uint8_t *__restrict__ q,
-                                             const float *__restrict__ q_scale,
-                                             const int32_t *__restrict__ seq_lens, int32_t qlen,
-                                             int b, int lane, int m, int g)
+                                             const float *__restrict__ q_scale, int32_t seq,
+                                             int32_t qlen, int b, int lane, int m, int g)
 {
-    const int32_t seq = seq_lens[b];
     bool nan_half[2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
@@ -161,6 +168,7 @@ __device__ __forceinline__ void load_request(RequestRegs &rq, const uint8_t *__r
 
 // Score one page for the 32 rows of the current request; returns the page-NaN flag
 // through `page_nan` and the per-lane maxima in r0 (row m) and r1 (row 16+m).
+template <bool kGeneral>
 __device__ __forceinline__ void score_page(const PageRegs &p, const uint64_t *lut,
                                            const RequestRegs &rq, float &r0, float &r1,
                                            bool &page_nan)
@@ -178,12 +186,16 @@ __device__ __forceinline__ void score_page(const PageRegs &p, const uint64_t *lu
         for (int hh = 0; hh < 2; ++hh) {
             const uint32_t s = (p.sc[t] >> (8 * hh)) & 0xFFu;
             const uint64_t e = lut[s];
-            const uint32_t flip = scale_sign_flip(s);
-            nan |= scale_is_nan(s);
+            uint32_t flip = 0;
+            if (kGeneral) {
+                flip = scale_sign_flip(s);
+                nan |= scale_is_nan(s);
+            }
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 uint32_t ev, od;
-                dequant_word(w[2 * hh + k] ^ flip, uint32_t(e >> 32), uint32_t(e), ev, od);
+                dequant_word(kGeneral ? w[2 * hh + k] ^ flip : w[2 * hh + k], uint32_t(e >> 32),
+                             uint32_t(e), ev, od);
                 const v8h av = __builtin_bit_cast(v8h, f16_word(ev, od));
                 c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                     av, __builtin_bit_cast(v8h, rq.qa[2 * hh + k]), c0, 0, 0, 0);
@@ -205,143 +217,92 @@ __device__ __forceinline__ void score_page(const PageRegs &p, const uint64_t *lu
     m1 = fmaxf(m1, __shfl_xor(m1, 32));
     r0 = m0;
     r1 = m1;
-    page_nan = __any(nan);
+    page_nan = kGeneral ? __any(nan) : false;
+}
+
+// True when some scale byte of the page (in any lane) is negative or NaN,
+// i.e. not in 0x00..0x7E: then the page takes the general path.
+__device__ __forceinline__ bool page_needs_general(const PageRegs &p)
+{
+    uint32_t f = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+        f |= p.sc[t] | (p.sc[t] + 0x0101u);   // bit 7 of a byte: byte >= 0x7F
+    return __any((f & 0x8080u) != 0);
 }
 
 __global__ __launch_bounds__(256) void score_decode_kernel(
     const uint8_t *__restrict__ kv, int64_t page_stride, int64_t num_blocks,
     const int32_t *__restrict__ block_table, int64_t bt_stride,
     const int32_t *__restrict__ seq_lens, const uint8_t *__restrict__ q,
-    const float *__restrict__ q_scale, int32_t num_reqs, int32_t qlen, int32_t width,
+    const float *__restrict__ q_scale, int32_t qlen, int32_t width, int32_t chunk,
     float *__restrict__ scores, int32_t *__restrict__ row_own)
 {
     __shared__ uint64_t lut[256];
-    __shared__ int32_t partial[256];
-    extern __shared__ int32_t prefix[];   // num_reqs + 1 entries
     const int tid = threadIdx.x;
-    load_lut_to_lds(lut);
-
-    // Own page of every row of every request (-1 for rows without a query).
-    if (row_own) {
-        for (int64_t i = (int64_t)blockIdx.x * 256 + tid; i < (int64_t)num_reqs * kDecodeRows;
-             i += (int64_t)gridDim.x * 256)
-            row_own[i] = decode_own(seq_lens[i / kDecodeRows], qlen,
-                                    (int)(i % kDecodeRows) / kDecodeHeads);
-    }
-
-    // Exclusive prefix sum of the pages scored per request.
-    const int per = (num_reqs + 255) / 256;
-    const int rb = tid * per;
-    const int re = rb + per < num_reqs ? rb + per : num_reqs;
-    int local = 0;
-    for (int r = rb; r < re; ++r)
-        local += pages_scored(seq_lens[r], width);
-    partial[tid] = local;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-        const int v = tid >= off ? partial[tid - off] : 0;
-        __syncthreads();
-        partial[tid] += v;
-        __syncthreads();
-    }
-    int run = partial[tid] - local;
-    for (int r = rb; r < re; ++r) {
-        prefix[r] = run;
-        run += pages_scored(seq_lens[r], width);
-    }
-    if (tid == 255)
-        prefix[num_reqs] = partial[255];
-    __syncthreads();
-
-    const int64_t total = prefix[num_reqs];
     const int wave = tid / kWave;
     const int lane = tid % kWave;
     const int m = lane & 15;
     const int g = lane >> 4;
-    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-    const int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-    const int64_t base = total / nwaves, rem = total % nwaves;
-    int64_t p = w * base + (w < rem ? w : rem);
-    const int64_t pend = p + base + (w < rem ? 1 : 0);
-    if (p >= pend)
+    const int b = blockIdx.y;
+    const int j0 = (blockIdx.x * kWavesPerBlock + wave) * chunk;
+
+    // First round of loads, all independent: the table, the request's length,
+    // the run's page ids (in bounds whatever the length: columns below the
+    // width) and the query rows.
+    load_lut_to_lds(lut);
+    const int32_t seq = seq_lens[b];
+    int32_t id_lane = -1;
+    if (lane < chunk && j0 + lane < width)
+        id_lane = block_table[(int64_t)b * bt_stride + j0 + lane];
+    RequestRegs rq;
+    load_request(rq, q, q_scale, seq, qlen, b, lane, m, g);
+    if (blockIdx.x == 0 && wave == 0 && row_own && lane < kDecodeRows)
+        row_own[(int64_t)b * kDecodeRows + lane] = rq.own;
+    __syncthreads();
+
+    const int np = pages_scored(seq, width);
+    const int j1 = j0 + chunk < np ? j0 + chunk : np;
+    if (j0 >= j1)
         return;
 
-    // Request holding flattened page p: prefix[b] <= p < prefix[b + 1].
-    auto find_req = [&](int64_t pp) {
-        int lo = 0, hi = num_reqs;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (prefix[mid] <= pp)
-                lo = mid;
-            else
-                hi = mid;
-        }
-        return lo;
+    // Source of page j; a page whose id is out of range is read from page 0
+    // instead (and not scored), so every step issues the same loads.
+    auto page_src = [&](int j, bool &ok) -> const uint8_t * {
+        const int64_t id = __shfl(id_lane, j - j0);
+        ok = id >= 0 && id < num_blocks;
+        return kv + (ok ? id : 0) * page_stride;
     };
-    // Lane i caches the page id of flattened page cache_base + i.
-    int64_t cache_base = p;
-    auto fill_cache = [&](int64_t cb) {
-        const int64_t pl = cb + lane;
-        int32_t id = -1;
-        if (pl < pend) {
-            const int bl = find_req(pl);
-            id = block_table[(int64_t)bl * bt_stride + (pl - prefix[bl])];
-        }
-        return id;
-    };
-    int32_t id_cache = fill_cache(cache_base);
-    auto page_id = [&](int64_t pp) -> int64_t {
-        return (int64_t)__shfl(id_cache, (int)(pp - cache_base));
-    };
-
-    int b = find_req(p);
-    int64_t bend = prefix[b + 1];
-    RequestRegs rq;
-    load_request(rq, q, q_scale, seq_lens, qlen, b, lane, m, g);
-
-    PageRegs cur, nxt;
-    int64_t id = page_id(p);
-    bool cur_ok = id >= 0 && id < num_blocks;
-    if (cur_ok)
-        fetch_page(cur, kv + id * page_stride, m, g);
-
-    for (;;) {
-        const int64_t pn = p + 1;
-        const bool has_next = pn < pend;
-        bool nxt_ok = false;
-        if (has_next) {
-            if (pn - cache_base >= kWave) {
-                cache_base = pn;
-                id_cache = fill_cache(cache_base);
-            }
-            const int64_t idn = page_id(pn);
-            nxt_ok = idn >= 0 && idn < num_blocks;
-            if (nxt_ok)
-                fetch_page(nxt, kv + idn * page_stride, m, g);
-        }
+    int j = j0;
+    // Issue the next page's loads (the current page again at the end of the
+    // run, a cache hit) into `nxt`, then score page j from `cur`.
+    auto step = [&](const PageRegs &cur, bool cur_ok, PageRegs &nxt, bool &nxt_ok) -> bool {
+        fetch_page(nxt, page_src(j + 1 < j1 ? j + 1 : j, nxt_ok), m, g);
         if (cur_ok) {
             float r0, r1;
             bool page_nan;
-            score_page(cur, lut, rq, r0, r1, page_nan);
-            const int j = (int)(p - prefix[b]);
+            if (page_needs_general(cur))
+                score_page<true>(cur, lut, rq, r0, r1, page_nan);
+            else
+                score_page<false>(cur, lut, rq, r0, r1, page_nan);
             if (lane < kDecodeRows && j < rq.own) {
                 const float v = lane < 16 ? r0 : r1;
-                float s = (v + fabsf(v)) * 0.5f * rq.qs;
+                float sc = (v + fabsf(v)) * 0.5f * rq.qs;
                 if (page_nan || rq.qnan)
-                    s = __builtin_nanf("");
-                scores[((int64_t)b * kDecodeRows + lane) * width + j] = s;
+                    sc = __builtin_nanf("");
+                scores[((int64_t)b * kDecodeRows + lane) * width + j] = sc;
             }
         }
-        if (!has_next)
+        return ++j < j1;
+    };
+    PageRegs pa, pb;
+    bool ok_a = false, ok_b = false;
+    fetch_page(pa, page_src(j, ok_a), m, g);
+    for (;;) {
+        if (!step(pa, ok_a, pb, ok_b))
             break;
-        p = pn;
-        if (p >= bend) {
-            b = find_req(p);
-            bend = prefix[b + 1];
-            load_request(rq, q, q_scale, seq_lens, qlen, b, lane, m, g);
-        }
-        cur = nxt;
-        cur_ok = nxt_ok;
+        if (!step(pb, ok_b, pa, ok_a))
+            break;
     }
 }
 
@@ -353,20 +314,16 @@ hipError_t launch_score_decode(const uint8_t *kv, int64_t page_stride, int64_t n
                                int32_t num_reqs, int32_t qlen, int32_t width, float *scores,
                                int32_t *row_own, int num_cus, hipStream_t stream)
 {
-    // Enough waves to cover the upper bound of the pages at two per wave, at
-    // most two blocks (eight waves, the occupancy the kernel's registers allow) per
-    // compute unit.
+    // Pages per wave: the batch's upper bound of pages spread over about eight
+    // waves per compute unit (two resident work-groups of four), 1..16.
     const int64_t max_pages = (int64_t)num_reqs * width;
-    int64_t blocks = (max_pages + 2 * kWavesPerBlock - 1) / (2 * kWavesPerBlock);
-    const int64_t cap = (int64_t)(num_cus > 0 ? num_cus : 256) * 2;
-    if (blocks > cap)
-        blocks = cap;
-    if (blocks < 1)
-        blocks = 1;
-    const size_t lds = sizeof(int32_t) * ((size_t)num_reqs + 1);
-    hipLaunchKernelGGL(score_decode_kernel, dim3((uint32_t)blocks), dim3(256), lds, stream, kv,
-                       page_stride, num_blocks, block_table, bt_stride, seq_lens, q, q_scale,
-                       num_reqs, qlen, width, scores, row_own);
+    const int64_t waves = (int64_t)(num_cus > 0 ? num_cus : 256) * 8;
+    int64_t chunk = (max_pages + waves - 1) / waves;
+    chunk = chunk < 1 ? 1 : (chunk > 16 ? 16 : chunk);
+    const int64_t gx = ((int64_t)width + chunk * kWavesPerBlock - 1) / (chunk * kWavesPerBlock);
+    hipLaunchKernelGGL(score_decode_kernel, dim3((uint32_t)gx, (uint32_t)num_reqs), dim3(256), 0,
+                       stream, kv, page_stride, num_blocks, block_table, bt_stride, seq_lens, q,
+                       q_scale, qlen, width, (int32_t)chunk, scores, row_own);
     return hipGetLastError();
 }
 

@@ -91,7 +91,7 @@ def _decode(lib, **kw):
 def test_decode_host_checks(lib):
     assert _decode(lib, R=0) == 0
     assert _decode(lib, R=-3) == EINVAL
-    assert _decode(lib, R=8193) == EINVAL                # beyond the per-call request limit
+    assert _decode(lib, R=65536) == EINVAL               # beyond the per-call request limit
     assert _decode(lib, qlen=0) == EINVAL
     assert _decode(lib, qlen=9) == EINVAL
     assert _decode(lib, W=0) == EINVAL
