@@ -63,21 +63,33 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int kWavesPerBlock = 4;
+constexpr int kXcds = 8;   // accelerator complex dies of an MI355X, each with its own L2
 
 struct PageRegs {
     u32x4 codes[8];   // per tile: 16 code bytes of token 16*tile + m, chunk g
-    uint32_t sc[8];   // per tile: the 2 scale bytes of that chunk
+    u32x4 scales;     // bytes 16*lane .. 16*lane+15 of the page's 1 KiB of scales
 };
 
-__device__ __forceinline__ void fetch_page(PageRegs &p, const uint8_t *src, int m, int g)
+// One page: eight 16-byte code loads per lane (1 KiB per wave each) and one
+// coalesced 16-byte load per lane of the scale block.
+__device__ __forceinline__ void fetch_page(PageRegs &p, const uint8_t *src, int lane, int m, int g)
 {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const int tok = 16 * t + m;
+    for (int t = 0; t < 8; ++t)
         p.codes[t] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4 *>(src + tok * 64 + 16 * g));
-        p.sc[t] = *reinterpret_cast<const uint16_t *>(src + kCodeBytes + tok * 8 + 2 * g);
-    }
+            reinterpret_cast<const u32x4 *>(src + (16 * t + m) * 64 + 16 * g));
+    p.scales = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + kCodeBytes + 16 * lane));
+}
+
+// The 2 scale bytes of tile t for this lane (token 16*t + m, groups 2g and
+// 2g+1), gathered through the wave's 1 KiB LDS staging area.
+__device__ __forceinline__ void unpack_scales(const PageRegs &p, uint8_t *stage, int lane, int m,
+                                              int g, uint32_t sc[8])
+{
+    *reinterpret_cast<u32x4 *>(stage + 16 * lane) = p.scales;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+        sc[t] = *reinterpret_cast<const uint16_t *>(stage + (16 * t + m) * 8 + 2 * g);
 }
 
 // E4M3 bytes [0,2,4,6] and [1,3,5,7] of a word -> the four f16 pairs (0,2) (4,6) (1,3) (5,7).
@@ -118,36 +130,54 @@ __device__ __forceinline__ int32_t pages_scored(int32_t seq, int32_t width)
 
 struct RequestRegs {
     u32x4 qa[4], qb[4];  // B operands (f16): query rows m and 16+m, chunk g, per code word
-    int own;          // lanes 0..31: own page of row `lane`
-    float qs;         // lanes 0..31: q_scale of row `lane`
-    bool qnan;        // lanes 0..31: row `lane` has a NaN query byte
+    int own;             // lanes 0..31: own page of row `lane`
+    float qs;            // lanes 0..31: q_scale of row `lane`
+    bool qnan;           // lanes 0..31: row `lane` has a NaN query byte
 };
 
-__device__ __forceinline__ void load_request(RequestRegs &rq, const uint8_t *__restrict__ q,
-                                             const float *__restrict__ q_scale, int32_t seq,
-                                             int32_t qlen, int b, int lane, int m, int g)
+// Raw query bytes (rows m and 16+m, depth chunk g) and the q_scale of row
+// `lane`, as loaded; slots without a query are not read.
+struct RequestRaw {
+    uint32_t bytes[2][8];
+    float qs;
+};
+
+__device__ __forceinline__ void load_request_raw(RequestRaw &r, const uint8_t *__restrict__ q,
+                                                 const float *__restrict__ q_scale, int32_t qlen,
+                                                 int b, int lane, int m, int g)
+{
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const int row = 16 * hf + m;
+        uint4 u0 = make_uint4(0u, 0u, 0u, 0u), u1 = u0;
+        if (row / kDecodeHeads >= kSlots - qlen) {
+            const uint4 *src =
+                reinterpret_cast<const uint4 *>(q + ((int64_t)b * kDecodeRows + row) * kDepth + 32 * g);
+            u0 = src[0];
+            u1 = src[1];
+        }
+        const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            r.bytes[hf][i] = w[i];
+    }
+    r.qs = 0.0f;
+    if (lane < kDecodeRows && lane / kDecodeHeads >= kSlots - qlen)
+        r.qs = q_scale[(int64_t)b * kDecodeRows + lane];
+}
+
+__device__ __forceinline__ void finish_request(RequestRegs &rq, const RequestRaw &r, int32_t seq,
+                                               int32_t qlen, int lane)
 {
     bool nan_half[2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-        const int row = 16 * hf + m;
-        const int slot = row / kDecodeHeads;
         u32x4 *dst = hf == 0 ? rq.qa : rq.qb;
         bool nan = false;
-        if (slot >= kSlots - qlen) {
-            const uint4 *src =
-                reinterpret_cast<const uint4 *>(q + ((int64_t)b * kDecodeRows + row) * kDepth + 32 * g);
-            const uint4 u0 = src[0], u1 = src[1];
-            const uint32_t raw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                dst[k] = q_word_f16(raw[2 * k], raw[2 * k + 1]);
-                nan |= has_nan_byte(raw[2 * k]) | has_nan_byte(raw[2 * k + 1]);
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                dst[k] = u32x4{0u, 0u, 0u, 0u};
+        for (int k = 0; k < 4; ++k) {
+            dst[k] = q_word_f16(r.bytes[hf][2 * k], r.bytes[hf][2 * k + 1]);
+            nan |= has_nan_byte(r.bytes[hf][2 * k]) | has_nan_byte(r.bytes[hf][2 * k + 1]);
         }
         // A row is NaN when any of its four depth chunks (lanes m, m+16, m+32, m+48) is.
         int f = nan ? 1 : 0;
@@ -157,7 +187,7 @@ __device__ __forceinline__ void load_request(RequestRegs &rq, const uint8_t *__r
     }
     if (lane < kDecodeRows) {
         rq.own = decode_own(seq, qlen, lane / kDecodeHeads);
-        rq.qs = rq.own >= 0 ? q_scale[(int64_t)b * kDecodeRows + lane] : 0.0f;
+        rq.qs = r.qs;
         rq.qnan = lane < 16 ? nan_half[0] : nan_half[1];
     } else {
         rq.own = -1;
@@ -166,12 +196,13 @@ __device__ __forceinline__ void load_request(RequestRegs &rq, const uint8_t *__r
     }
 }
 
-// Score one page for the 32 rows of the current request; returns the page-NaN flag
-// through `page_nan` and the per-lane maxima in r0 (row m) and r1 (row 16+m).
+// Score one page for the request's 32 rows: the per-lane maxima r0 (row m)
+// and r1 (row 16+m) of the raw dot products, and whether a NaN scale byte
+// makes the whole page NaN.
 template <bool kGeneral>
-__device__ __forceinline__ void score_page(const PageRegs &p, const uint64_t *lut,
-                                           const RequestRegs &rq, float &r0, float &r1,
-                                           bool &page_nan)
+__device__ __forceinline__ void score_page(const PageRegs &p, const uint32_t sc[8],
+                                           const uint64_t *lut, const RequestRegs &rq, float &r0,
+                                           float &r1, bool &page_nan)
 {
     const float ninf = -__builtin_huge_valf();
     v4f mx0 = {ninf, ninf, ninf, ninf};
@@ -179,12 +210,16 @@ __device__ __forceinline__ void score_page(const PageRegs &p, const uint64_t *lu
     bool nan = false;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
+        // The fence keeps the compiler from hoisting the selector arithmetic
+        // of all eight tiles to the top of the page, which would hold dozens
+        // of registers live at once.
+        __builtin_amdgcn_sched_barrier(0);
         const uint32_t w[4] = {p.codes[t][0], p.codes[t][1], p.codes[t][2], p.codes[t][3]};
         v4f c0 = {0.f, 0.f, 0.f, 0.f};
         v4f c1 = c0;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            const uint32_t s = (p.sc[t] >> (8 * hh)) & 0xFFu;
+            const uint32_t s = (sc[t] >> (8 * hh)) & 0xFFu;
             const uint64_t e = lut[s];
             uint32_t flip = 0;
             if (kGeneral) {
@@ -209,6 +244,7 @@ __device__ __forceinline__ void score_page(const PageRegs &p, const uint64_t *lu
             mx1[i] = fmaxf(mx1[i], c1[i]);
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
     float m0 = fmaxf(fmaxf(mx0[0], mx0[1]), fmaxf(mx0[2], mx0[3]));
     float m1 = fmaxf(fmaxf(mx1[0], mx1[1]), fmaxf(mx1[2], mx1[3]));
     m0 = fmaxf(m0, __shfl_xor(m0, 16));
@@ -220,18 +256,20 @@ __device__ __forceinline__ void score_page(const PageRegs &p, const uint64_t *lu
     page_nan = kGeneral ? __any(nan) : false;
 }
 
-// True when some scale byte of the page (in any lane) is negative or NaN,
-// i.e. not in 0x00..0x7E: then the page takes the general path.
+// True when some scale byte of the page is negative or NaN, i.e. not in
+// 0x00..0x7E: then the page takes the general path.  Per byte, bit 7 of
+// byte | (byte + 1) is set exactly when byte >= 0x7F; a carry out of a 0xFF
+// byte can only flag its neighbour as well, which merely costs the fast path.
 __device__ __forceinline__ bool page_needs_general(const PageRegs &p)
 {
     uint32_t f = 0;
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-        f |= p.sc[t] | (p.sc[t] + 0x0101u);   // bit 7 of a byte: byte >= 0x7F
-    return __any((f & 0x8080u) != 0);
+    for (int i = 0; i < 4; ++i)
+        f |= p.scales[i] | (p.scales[i] + 0x01010101u);
+    return __any((f & 0x80808080u) != 0);
 }
 
-__global__ __launch_bounds__(256) void score_decode_kernel(
+__global__ __launch_bounds__(256, 2) void score_decode_kernel(
     const uint8_t *__restrict__ kv, int64_t page_stride, int64_t num_blocks,
     const int32_t *__restrict__ block_table, int64_t bt_stride,
     const int32_t *__restrict__ seq_lens, const uint8_t *__restrict__ q,
@@ -239,65 +277,90 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
     float *__restrict__ scores, int32_t *__restrict__ row_own)
 {
     __shared__ uint64_t lut[256];
+    __shared__ __align__(16) uint8_t scale_stage[kWavesPerBlock][1024];
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int lane = tid % kWave;
     const int m = lane & 15;
     const int g = lane >> 4;
-    const int b = blockIdx.y;
-    const int j0 = (blockIdx.x * kWavesPerBlock + wave) * chunk;
+    // XCD-aware block order.  Work-groups are dispatched round-robin over the
+    // eight XCDs, each with its own L2.  Renumbering so that every XCD gets a
+    // contiguous range of (request, run) blocks keeps the columns a row's
+    // 128-byte score lines share inside one L2, which then writes whole lines
+    // back instead of four partial ones from four XCDs.
+    const int gx = gridDim.x;
+    const int total = gx * gridDim.y;
+    const int lin = blockIdx.x + blockIdx.y * gx;
+    const int xcd = lin % kXcds, slot = lin / kXcds;
+    const int per = total / kXcds, extra = total % kXcds;
+    const int logical = xcd < extra ? xcd * (per + 1) + slot : extra * (per + 1) + (xcd - extra) * per + slot;
+    const int b = logical / gx;
+    const int j0 = ((logical % gx) * kWavesPerBlock + wave) * chunk;
+    uint8_t *stage = scale_stage[wave];
 
-    // First round of loads, all independent: the table, the request's length,
-    // the run's page ids (in bounds whatever the length: columns below the
-    // width) and the query rows.
-    load_lut_to_lds(lut);
+    // First round of loads, all independent: the request's length, the run's
+    // page ids (in bounds whatever the length: columns below the width), the
+    // table and the query rows.  The first page is requested as soon as the
+    // length and the ids are in; the table, the query conversion and the
+    // barrier come after, while that page is in flight.
     const int32_t seq = seq_lens[b];
     int32_t id_lane = -1;
     if (lane < chunk && j0 + lane < width)
         id_lane = block_table[(int64_t)b * bt_stride + j0 + lane];
-    RequestRegs rq;
-    load_request(rq, q, q_scale, seq, qlen, b, lane, m, g);
-    if (blockIdx.x == 0 && wave == 0 && row_own && lane < kDecodeRows)
-        row_own[(int64_t)b * kDecodeRows + lane] = rq.own;
-    __syncthreads();
+    const uint64_t lut_entry_g = kNvfp4Lut.entry[tid];
+    RequestRaw qraw;
+    load_request_raw(qraw, q, q_scale, qlen, b, lane, m, g);
 
     const int np = pages_scored(seq, width);
     const int j1 = j0 + chunk < np ? j0 + chunk : np;
-    if (j0 >= j1)
-        return;
 
     // Source of page j; a page whose id is out of range is read from page 0
     // instead (and not scored), so every step issues the same loads.
+    // The id is read with v_readlane, so the page base is a scalar and every
+    // load uses it with a constant per-lane offset.
     auto page_src = [&](int j, bool &ok) -> const uint8_t * {
-        const int64_t id = __shfl(id_lane, j - j0);
+        const int64_t id = __builtin_amdgcn_readlane(id_lane, j - j0);
         ok = id >= 0 && id < num_blocks;
         return kv + (ok ? id : 0) * page_stride;
     };
+    PageRegs pa, pb;
+    bool ok_a = false, ok_b = false;
+    if (j0 < j1)
+        fetch_page(pa, page_src(j0, ok_a), lane, m, g);
+
+    lut[tid] = lut_entry_g;
+    RequestRegs rq;
+    finish_request(rq, qraw, seq, qlen, lane);
+    if (logical % gx == 0 && wave == 0 && row_own && lane < kDecodeRows)
+        row_own[(int64_t)b * kDecodeRows + lane] = rq.own;
+    __syncthreads();
+    if (j0 >= j1)
+        return;
+
     int j = j0;
     // Issue the next page's loads (the current page again at the end of the
     // run, a cache hit) into `nxt`, then score page j from `cur`.
     auto step = [&](const PageRegs &cur, bool cur_ok, PageRegs &nxt, bool &nxt_ok) -> bool {
-        fetch_page(nxt, page_src(j + 1 < j1 ? j + 1 : j, nxt_ok), m, g);
+        fetch_page(nxt, page_src(j + 1 < j1 ? j + 1 : j, nxt_ok), lane, m, g);
         if (cur_ok) {
+            uint32_t sc[8];
+            unpack_scales(cur, stage, lane, m, g, sc);
             float r0, r1;
             bool page_nan;
             if (page_needs_general(cur))
-                score_page<true>(cur, lut, rq, r0, r1, page_nan);
+                score_page<true>(cur, sc, lut, rq, r0, r1, page_nan);
             else
-                score_page<false>(cur, lut, rq, r0, r1, page_nan);
+                score_page<false>(cur, sc, lut, rq, r0, r1, page_nan);
             if (lane < kDecodeRows && j < rq.own) {
                 const float v = lane < 16 ? r0 : r1;
-                float sc = (v + fabsf(v)) * 0.5f * rq.qs;
+                float s = (v + fabsf(v)) * 0.5f * rq.qs;
                 if (page_nan || rq.qnan)
-                    sc = __builtin_nanf("");
-                scores[((int64_t)b * kDecodeRows + lane) * width + j] = sc;
+                    s = __builtin_nanf("");
+                scores[((int64_t)b * kDecodeRows + lane) * width + j] = s;
             }
         }
         return ++j < j1;
     };
-    PageRegs pa, pb;
-    bool ok_a = false, ok_b = false;
-    fetch_page(pa, page_src(j, ok_a), m, g);
     for (;;) {
         if (!step(pa, ok_a, pb, ok_b))
             break;
