@@ -44,7 +44,8 @@
 // wave issues its first loads -- the request's length, the run's page ids and
 // the query rows -- all at once, so a single memory round trip precedes the
 // first page fetch; then it scores the run with two page buffers in turn, the
-// next page's 9 KiB in flight while the current one is scored.  Runs past a
+// next page's 9 KiB in flight while the current one is scored (past the run's
+// end the loads go through an empty descriptor and cost nothing).  Runs past a
 // request's last page exit at once, and the hardware dispatcher back-fills the
 // compute units, which balances ragged batches.
 //
@@ -71,14 +72,33 @@ struct PageRegs {
 };
 
 // One page: eight 16-byte code loads per lane (1 KiB per wave each) and one
-// coalesced 16-byte load per lane of the scale block.
-__device__ __forceinline__ void fetch_page(PageRegs &p, const uint8_t *src, int lane, int m, int g)
+// coalesced 16-byte load per lane of the scale block, as buffer loads against
+// a descriptor that covers only this page.  A descriptor with no records
+// makes every load return zeros without touching memory, so a wave issues
+// the same loads for every page, whether it exists or not.
+constexpr int kStreamLoad = 2;   // cache policy: nontemporal (streamed once)
+
+// The fields go through v_readfirstlane: they are wave-uniform by
+// construction, and this keeps the descriptor in scalar registers (a
+// descriptor the compiler cannot prove uniform costs a loop per load).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t *page, bool live)
+{
+    const uint64_t a = reinterpret_cast<uintptr_t>(page);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const int records = __builtin_amdgcn_readfirstlane(live ? kPageBytes : 0);
+    return __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), (short)0, records, 0x00020000);
+}
+
+__device__ __forceinline__ void fetch_page(PageRegs &p, __amdgpu_buffer_rsrc_t src, int lane, int m,
+                                           int g)
 {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
-        p.codes[t] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4 *>(src + (16 * t + m) * 64 + 16 * g));
-    p.scales = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + kCodeBytes + 16 * lane));
+        p.codes[t] = __builtin_amdgcn_raw_buffer_load_b128(src, (16 * t + m) * 64 + 16 * g, 0,
+                                                           kStreamLoad);
+    p.scales = __builtin_amdgcn_raw_buffer_load_b128(src, kCodeBytes + 16 * lane, 0, kStreamLoad);
 }
 
 // The 2 scale bytes of tile t for this lane (token 16*t + m, groups 2g and
@@ -314,14 +334,14 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
     const int np = pages_scored(seq, width);
     const int j1 = j0 + chunk < np ? j0 + chunk : np;
 
-    // Source of page j; a page whose id is out of range is read from page 0
-    // instead (and not scored), so every step issues the same loads.
-    // The id is read with v_readlane, so the page base is a scalar and every
-    // load uses it with a constant per-lane offset.
-    auto page_src = [&](int j, bool &ok) -> const uint8_t * {
+    // Descriptor of page j: empty past the run and for an id out of range
+    // (such a page is not scored).  The id is read with v_readlane, so the
+    // page base is a scalar and every load uses it with a constant per-lane
+    // offset.
+    auto page_src = [&](int j, bool &ok) -> __amdgpu_buffer_rsrc_t {
         const int64_t id = __builtin_amdgcn_readlane(id_lane, j - j0);
-        ok = id >= 0 && id < num_blocks;
-        return kv + (ok ? id : 0) * page_stride;
+        ok = j < j1 && id >= 0 && id < num_blocks;
+        return page_rsrc(kv + (ok ? id : 0) * page_stride, ok);
     };
     PageRegs pa, pb;
     bool ok_a = false, ok_b = false;
@@ -338,10 +358,11 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
         return;
 
     int j = j0;
-    // Issue the next page's loads (the current page again at the end of the
-    // run, a cache hit) into `nxt`, then score page j from `cur`.
+    // Issue the next page's loads into `nxt` (after the run's last page the
+    // descriptor is empty and the loads cost nothing), then score page j
+    // from `cur`.
     auto step = [&](const PageRegs &cur, bool cur_ok, PageRegs &nxt, bool &nxt_ok) -> bool {
-        fetch_page(nxt, page_src(j + 1 < j1 ? j + 1 : j, nxt_ok), lane, m, g);
+        fetch_page(nxt, page_src(j + 1 < j1 ? j + 1 : j1, nxt_ok), lane, m, g);
         if (cur_ok) {
             uint32_t sc[8];
             unpack_scales(cur, stage, lane, m, g, sc);
