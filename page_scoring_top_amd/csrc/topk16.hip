@@ -15,26 +15,28 @@
 //
 // Work split (the exact merge of the vLLM page's module description: the best
 // 16 of a row lie in the union of the best 16 of any partition of its
-// columns).  A row is cut into 1..16 contiguous partitions, one wave each, in
-// one work-group; each wave streams its columns in passes of 256 (4 per lane)
-// and keeps its best 16 so far, one key per lane in lanes 0..15.  At the end
-// the row's first wave selects the best 16 of the partitions' results.
+// columns).  A row is cut into 1, 2 or 4 contiguous partitions, one wave each
+// and one per SIMD of the work-group.  A wave holds up to 1,024 of its columns
+// in registers (16 per lane) and keeps its best 16 so far, one key per lane in
+// lanes 0..15; wider partitions take several such passes.  The row's first
+// wave then merges the partitions' sorted results, at most 64 keys, one per
+// lane, with the last steps of a bitonic sort.
 //
-// Selection of the best 16 among a few keys per lane, as the MSA pull request
-// describes it for a 32-lane warp, here on 64 lanes: (1) each lane takes the
-// maximum of its keys; (2) the largest high word t such that at least 16 lane
-// maxima reach it is found by a most-significant-bits-first search whose
-// counts are ballots; (3) every key whose high word reaches t survives -- the
-// 16 lanes whose maxima reach t hold 16 distinct keys no smaller than any key
-// below t, so the best 16 are among the survivors; (4) survivors are compacted
-// into LDS (ballot prefix counts) and each is ranked by counting the survivors
-// above it.  When more than 64 keys survive (ties in the score), the exact
-// 16th key is found by a 64-bit bisection over all the keys instead, and
-// exactly 16 survive.
+// Selection of the best 16 among a few keys per lane, after the MSA pull
+// request's warp scheme, here on 64 lanes: (1) each lane takes the maximum of
+// its keys' high words; (2) a bitonic sort of those 64 maxima across the wave
+// (DPP row and quad moves and the permlane swaps; no LDS) gives t, the 16th
+// largest; (3) every key whose high word reaches t survives -- the 16 lanes
+// whose maxima reach t hold 16 distinct keys no smaller than any key below t,
+// so the best 16 are among the survivors; (4) the survivors are compacted one
+// per lane through LDS (ballot prefix counts) and sorted by a second bitonic
+// sort on the full keys.  When more than 64 keys survive (ties in the score),
+// the exact 16th key is found by a 64-bit bisection over all the keys
+// instead, and exactly 16 survive.
 //
-// In a pass, a new key at or below the wave's current 16th key cannot enter
-// its best 16 and is dropped before selection; a pass that keeps no new key
-// costs one compare and ballot per slot.
+// In a pass, a new key whose high word is below that of the wave's current
+// 16th key cannot enter its best 16 and is dropped before selection; a pass
+// that keeps no new key costs one compare and ballot per slot.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -42,12 +44,13 @@ namespace pagescore {
 
 namespace {
 
-constexpr int kMaxWavesPerRow = 16;
-constexpr int kPerLane = 4;                        // new keys per lane and pass
-constexpr int kPassCols = kPerLane * kWave;        // 256 columns per pass
-constexpr int kBlockWaves = 16;                    // waves per work-group (rows x partitions)
+constexpr int kMaxWavesPerRow = 4;
+constexpr int kWideLane = 16;                      // columns per lane and pass (1,024 per wave)
+constexpr int kNarrowLane = 4;                     // for rows of at most 256 columns
+constexpr int kBlockWaves = 4;                     // one wave per SIMD
 
-__device__ __forceinline__ uint64_t make_key(float s, int col, int fb, int fe)
+// Order-preserving image of the canonical score (never 0).
+__device__ __forceinline__ uint32_t key_hi(float s, int col, int fb, int fe)
 {
     uint32_t u = __float_as_uint(s);
     if (col >= fb && col < fe)
@@ -56,8 +59,12 @@ __device__ __forceinline__ uint64_t make_key(float s, int col, int fb, int fe)
         u = 0xFF800000u;                       // NaN: -inf
     else if (u == 0x80000000u)
         u = 0u;                                // -0: +0
-    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)col);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t make_key(uint32_t hi, int col)
+{
+    return ((uint64_t)hi << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)col);
 }
 
 __device__ __forceinline__ int key_col(uint64_t key)
@@ -70,6 +77,13 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l)
     const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
     const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
     return ((uint64_t)hi << 32) | lo;
+}
+
+// Number of lanes set in a ballot, as a 32-bit count (keeps the comparisons
+// that follow on the scalar unit).
+__device__ __forceinline__ int lanes_set(uint64_t mask)
+{
+    return __builtin_popcount((uint32_t)mask) + __builtin_popcount((uint32_t)(mask >> 32));
 }
 
 // Set bits of `mask` below this lane.
@@ -88,146 +102,261 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// The 16 largest keys among key[0..N) of all 64 lanes (0 = empty slot).
-// Returns the r-th largest in lane r < 16 (0 when there are fewer than r + 1
-// keys) and 0 in lanes 16..63.  `surv` (64 keys) and `res` (16 keys) are the
-// wave's LDS scratch.
-template <int N>
-__device__ __forceinline__ uint64_t wave_top16(const uint64_t (&key)[N], uint64_t *surv,
-                                               uint64_t *res, int lane)
+// The value of lane (lane ^ J).  J = 1, 2: quad permutes; J = 4: row shift
+// left or right by 4; J = 8: row rotate by 8; J = 16, 32: the gfx950 permlane
+// swaps, which hand each lane both halves of the exchange.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x, int lane)
 {
-    uint64_t lmax = 0;
+    if constexpr (J == 1) {
+        return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    } else if constexpr (J == 2) {
+        return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    } else if constexpr (J == 4) {
+        const uint32_t from_above = __builtin_amdgcn_mov_dpp(x, 0x104, 0xF, 0xF, false);  // row_shl:4
+        const uint32_t from_below = __builtin_amdgcn_mov_dpp(x, 0x114, 0xF, 0xF, false);  // row_shr:4
+        return (lane & 4) ? from_below : from_above;
+    } else if constexpr (J == 8) {
+        return __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror:8
+    } else if constexpr (J == 16) {
+        const auto s = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (lane & 16) ? s[0] : s[1];
+    } else {
+        static_assert(J == 32, "xor distance");
+        const auto s = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (lane & 32) ? s[0] : s[1];
+    }
+}
+
+// One compare-exchange step of a descending bitonic sort over 64 lanes:
+// merge blocks of K lanes at distance J.  The lane keeps the larger value of
+// the pair when its position in the block says so, else the smaller one
+// (equal values are interchangeable).
+template <int K, int J, typename T>
+__device__ __forceinline__ T bitonic_step(T x, int lane)
+{
+    T y;
+    if constexpr (sizeof(T) == 4) {
+        y = xor_lane<J>(x, lane);
+    } else {
+        const uint32_t ylo = xor_lane<J>((uint32_t)x, lane);
+        const uint32_t yhi = xor_lane<J>((uint32_t)(x >> 32), lane);
+        y = ((uint64_t)yhi << 32) | ylo;
+    }
+    const bool keep_max = ((lane & J) == 0) == ((lane & K) == 0 || K == 64);
+    return ((y > x) == keep_max) ? y : x;
+}
+
+// Descending sort of one value per lane across the wave: lane 0 ends with
+// the largest.
+template <typename T>
+__device__ __forceinline__ T wave_sort_desc(T x, int lane)
+{
+    x = bitonic_step<2, 1>(x, lane);
+    x = bitonic_step<4, 2>(x, lane);
+    x = bitonic_step<4, 1>(x, lane);
+    x = bitonic_step<8, 4>(x, lane);
+    x = bitonic_step<8, 2>(x, lane);
+    x = bitonic_step<8, 1>(x, lane);
+    x = bitonic_step<16, 8>(x, lane);
+    x = bitonic_step<16, 4>(x, lane);
+    x = bitonic_step<16, 2>(x, lane);
+    x = bitonic_step<16, 1>(x, lane);
+    x = bitonic_step<32, 16>(x, lane);
+    x = bitonic_step<32, 8>(x, lane);
+    x = bitonic_step<32, 4>(x, lane);
+    x = bitonic_step<32, 2>(x, lane);
+    x = bitonic_step<32, 1>(x, lane);
+    x = bitonic_step<64, 32>(x, lane);
+    x = bitonic_step<64, 16>(x, lane);
+    x = bitonic_step<64, 8>(x, lane);
+    x = bitonic_step<64, 4>(x, lane);
+    x = bitonic_step<64, 2>(x, lane);
+    x = bitonic_step<64, 1>(x, lane);
+    return x;
+}
+
+// Exclusive prefix sum of x over the lanes below (DPP row shifts within
+// each row of 16, then the rows' totals via the permlane swaps).
+__device__ __forceinline__ int wave_prefix_sum(int x, int lane)
+{
+    int v = x;   // inclusive sum within the row
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+        const int y = d == 1 ? __builtin_amdgcn_mov_dpp(v, 0x111, 0xF, 0xF, true)     // row_shr:1
+                    : d == 2 ? __builtin_amdgcn_mov_dpp(v, 0x112, 0xF, 0xF, true)     // row_shr:2
+                    : d == 4 ? __builtin_amdgcn_mov_dpp(v, 0x114, 0xF, 0xF, true)     // row_shr:4
+                             : __builtin_amdgcn_mov_dpp(v, 0x118, 0xF, 0xF, true);    // row_shr:8
+        v += (lane & 15) >= d ? y : 0;
+    }
+    // Row totals: lane 15 of each row.
+    const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+              r2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = lane >> 4;
+    const int below_rows = (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+    return v - x + below_rows;
+}
+
+// The candidates of one selection: N columns per lane given by their high
+// words (0 = empty) at columns base + 64 i + lane, plus up to 16 earlier
+// winners (`held`, one full key per lane in lanes 0..15).
+template <int N>
+struct Candidates {
+    uint32_t hi[N];
+    int base;
+    uint64_t held;
+};
+
+// Place the candidates that `keep` selects (slot -1 is the held key) one
+// per lane in surv[0..total) and return total; nothing is placed when more
+// than 64 are selected.  Each lane counts its own and a prefix sum across
+// the wave places them; a lane's unselected candidates go to a spare slot of
+// its own, so the stores need no branches.
+template <int N, typename Keep>
+__device__ __forceinline__ int place_survivors(const Candidates<N> &c, Keep keep, uint64_t *surv,
+                                               int lane)
+{
+    int mine = keep(-1) ? 1 : 0;
 #pragma unroll
     for (int i = 0; i < N; ++i)
-        lmax = key[i] > lmax ? key[i] : lmax;
-    const uint32_t lhi = (uint32_t)(lmax >> 32);
-    // Two bits per step: the three candidates' counts are independent.
-    uint32_t t = 0;
-    for (int sh = 30; sh >= 0; sh -= 2) {
-        const uint32_t c1 = t | (1u << sh), c2 = t | (2u << sh), c3 = t | (3u << sh);
-        const int n1 = __popcll(__ballot(lhi >= c1));
-        const int n2 = __popcll(__ballot(lhi >= c2));
-        const int n3 = __popcll(__ballot(lhi >= c3));
-        t = n3 >= kTopk ? c3 : (n2 >= kTopk ? c2 : (n1 >= kTopk ? c1 : t));
-    }
-    uint64_t mask[N];
-    int total = 0;
+        mine += keep(i) ? 1 : 0;
+    const int before = wave_prefix_sum(mine, lane);
+    const int total = __builtin_amdgcn_readlane(before + mine, kWave - 1);
+    if (total <= kWave) {
+        int pos = before;
+        const bool kh = keep(-1);
+        surv[kh ? pos : kWave + lane] = c.held;
+        pos += kh ? 1 : 0;
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-        mask[i] = __ballot(key[i] != 0 && (uint32_t)(key[i] >> 32) >= t);
-        total += __popcll(mask[i]);
+        for (int i = 0; i < N; ++i) {
+            const bool k = keep(i);
+            surv[k ? pos : kWave + lane] = make_key(c.hi[i], c.base + i * kWave + lane);
+            pos += k ? 1 : 0;
+        }
     }
+    return total;
+}
+
+// The 16 largest candidate keys, the r-th largest in lane r < 16 and 0 in
+// lanes 16..63 (0 also past the number of candidates).  `surv` is 128 keys
+// of the wave's LDS: 64 places for survivors and a spare slot per lane.
+template <int N>
+__device__ __forceinline__ uint64_t wave_top16(const Candidates<N> &c, uint64_t *surv, int lane)
+{
+    const uint32_t held_hi = (uint32_t)(c.held >> 32);
+    uint32_t lmax = held_hi;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        lmax = c.hi[i] > lmax ? c.hi[i] : lmax;
+    uint32_t t = __builtin_amdgcn_readlane(wave_sort_desc(lmax, lane), kTopk - 1);
+    t = t > 0 ? t : 1;   // real keys only
+
+    // Survivors: keys whose high word reaches t.
+    int total = place_survivors(
+        c, [&](int i) { return (i < 0 ? held_hi : c.hi[i]) >= t; }, surv, lane);
     if (total > kWave) {
-        // Exact 16th key (at least 16 keys exist: more than 64 survived).
+        // Ties on the high word: the exact 16th key (at least 16 keys exist,
+        // since more than 64 survived), and exactly 16 survivors.
         uint64_t kth = 0;
         for (int bit = 63; bit >= 0; --bit) {
             const uint64_t cand = kth | (1ull << bit);
-            int cnt = 0;
+            int cnt = lanes_set(__ballot(c.held >= cand));
 #pragma unroll
             for (int i = 0; i < N; ++i)
-                cnt += __popcll(__ballot(key[i] >= cand));
+                cnt += lanes_set(__ballot(c.hi[i] != 0 &&
+                                          make_key(c.hi[i], c.base + i * kWave + lane) >= cand));
             if (cnt >= kTopk)
                 kth = cand;
         }
-        total = 0;
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            mask[i] = __ballot(key[i] >= kth);
-            total += __popcll(mask[i]);
-        }
-    }
-    int base = 0;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        if ((mask[i] >> lane) & 1ull)
-            surv[base + bits_below(mask[i])] = key[i];
-        base += __popcll(mask[i]);
+        total = place_survivors(
+            c,
+            [&](int i) {
+                return i < 0 ? c.held >= kth
+                             : (c.hi[i] != 0 && make_key(c.hi[i], c.base + i * kWave + lane) >= kth);
+            },
+            surv, lane);
     }
     wave_lds_sync();
-    if (lane < total) {
-        const uint64_t mine = surv[lane];
-        int rank = 0;
-        for (int j = 0; j < total; ++j)
-            rank += surv[j] > mine ? 1 : 0;
-        if (rank < kTopk)
-            res[rank] = mine;
-    }
-    wave_lds_sync();
-    const int got = total < kTopk ? total : kTopk;
-    const uint64_t r = lane < got ? res[lane] : 0;
+    const uint64_t mine = lane < total ? surv[lane] : 0;
     wave_lds_sync();   // the scratch may be rewritten by the caller's next selection
-    return r;
+    const uint64_t sorted = wave_sort_desc(mine, lane);
+    return lane < kTopk ? sorted : 0;
 }
 
-__device__ __forceinline__ void load_pass(const float *srow, int c, int c1, float (&v)[kPerLane])
-{
-#pragma unroll
-    for (int i = 0; i < kPerLane; ++i)
-        v[i] = c + i * kWave < c1 ? srow[c + i * kWave] : 0.0f;
-}
-
-__global__ __launch_bounds__(1024) void topk16_kernel(
+template <int kPerLane>
+__global__ __launch_bounds__(256) void topk16_kernel(
     const float *__restrict__ scores, int64_t row_stride, int32_t num_rows, int32_t width,
     const int32_t *__restrict__ valid_len, const int32_t *__restrict__ force_begin,
     const int32_t *__restrict__ force_end, const int32_t *__restrict__ append_page,
     int32_t waves_per_row, int32_t *__restrict__ out, int64_t out_stride)
 {
-    __shared__ uint64_t surv[kBlockWaves][kWave];
-    __shared__ uint64_t res[kBlockWaves][kTopk];
+    constexpr int kPassCols = kPerLane * kWave;
+    __shared__ uint64_t surv[kBlockWaves][2 * kWave];
     __shared__ uint64_t part_best[kBlockWaves][kTopk];
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
-    const int rows_per_block = (int)(blockDim.x / kWave) / waves_per_row;
+    const int rows_per_block = kBlockWaves / waves_per_row;
     const int row_in_block = wave / waves_per_row;
     const int part = wave % waves_per_row;
     const int64_t row = (int64_t)blockIdx.x * rows_per_block + row_in_block;
     const bool live = row < num_rows;   // no early return: the work-group meets at a barrier
+    const float *srow = scores + (live ? row : 0) * row_stride;
 
-    // The row's parameters, all requested at once (the appended page too).
+    // This wave's columns: whole 64-column groups of the width, split evenly;
+    // the row's valid length trims them once it is known.  The first pass is
+    // requested together with the row's parameters (every lane loads every
+    // slot, a column past the end reading the last one, so the loads issue
+    // back to back with no branch between them).
+    const int groups = (width + kWave - 1) / kWave;
+    const int span = ((groups + waves_per_row - 1) / waves_per_row) * kWave;
+    const int c0 = part * span;
+    const int cw = live ? (c0 + span < width ? c0 + span : width) : c0;   // loadable end
+    auto load = [&](int pc, float (&v)[kPerLane]) {
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i) {
+            const int col = pc + i * kWave + lane;
+            v[i] = srow[col < cw ? col : cw - 1];
+        }
+    };
+    float v[kPerLane];
+    if (c0 < cw)
+        load(c0, v);
+
     int n = 0, fb = 0, fe = 0, ap = -1;
-    const float *srow = scores;
     if (live) {
         n = valid_len ? valid_len[row] : width;
         n = n < 0 ? 0 : (n > width ? width : n);
         fb = force_begin ? force_begin[row] : 0;
         fe = force_end ? force_end[row] : 0;
         ap = append_page ? append_page[row] : -1;
-        srow = scores + row * row_stride;
     }
-
-    // This wave's columns: whole 64-column groups, split evenly.
-    const int groups = (n + kWave - 1) / kWave;
-    const int span = ((groups + waves_per_row - 1) / waves_per_row) * kWave;
-    const int c0 = part * span;
-    const int c1 = c0 + span < n ? c0 + span : n;
+    const int c1 = cw < n ? cw : n;   // this wave's candidates: [c0, c1)
 
     uint64_t best = 0;   // lane r < 16: this partition's r-th best key so far
-    if (c0 < c1) {
-        float v[kPerLane];
-        load_pass(srow, c0 + lane, c1, v);
-        for (int pc = c0; pc < c1; pc += kPassCols) {
-            float nv[kPerLane];
-            if (pc + kPassCols < c1)
-                load_pass(srow, pc + kPassCols + lane, c1, nv);
-            const uint64_t floor_key = readlane_u64(best, kTopk - 1);
-            uint64_t key[kPerLane + 1];
-            bool any_new = false;
+    for (int pc = c0; pc < c1; pc += kPassCols) {
+        float nv[kPerLane];
+        if (pc + kPassCols < c1)
+            load(pc + kPassCols, nv);
+        Candidates<kPerLane> cand;
+        cand.base = pc;
+        cand.held = best;
+        // Keys whose high word is below the current 16th best cannot enter.
+        const uint32_t floor_hi = (uint32_t)(readlane_u64(best, kTopk - 1) >> 32);
+        bool any_new = false;
 #pragma unroll
-            for (int i = 0; i < kPerLane; ++i) {
-                const int c = pc + lane + i * kWave;
-                uint64_t k = c < c1 ? make_key(v[i], c, fb, fe) : 0;
-                k = k > floor_key ? k : 0;
-                any_new |= k != 0;
-                key[i] = k;
-            }
-            key[kPerLane] = best;
-            if (__any(any_new))
-                best = wave_top16(key, surv[wave], res[wave], lane);
-            if (pc + kPassCols < c1) {
+        for (int i = 0; i < kPerLane; ++i) {
+            const int col = pc + i * kWave + lane;
+            uint32_t h = col < c1 ? key_hi(v[i], col, fb, fe) : 0u;
+            h = h >= floor_hi ? h : 0u;
+            any_new |= h != 0;
+            cand.hi[i] = h;
+        }
+        if (__any(any_new))
+            best = wave_top16(cand, surv[wave], lane);
+        if (pc + kPassCols < c1) {
 #pragma unroll
-                for (int i = 0; i < kPerLane; ++i)
-                    v[i] = nv[i];
-            }
+            for (int i = 0; i < kPerLane; ++i)
+                v[i] = nv[i];
         }
     }
 
@@ -237,14 +366,25 @@ __global__ __launch_bounds__(1024) void topk16_kernel(
             part_best[wave][lane] = best;
         __syncthreads();
         if (part == 0) {
-            // Partition results of this row: waves_per_row * 16 <= 256 keys, 4 per lane.
-            const uint64_t *pb = &part_best[wave][0];
-            const int cnt = waves_per_row * kTopk;
-            uint64_t key[kPerLane];
-#pragma unroll
-            for (int i = 0; i < kPerLane; ++i)
-                key[i] = lane + i * kWave < cnt ? pb[lane + i * kWave] : 0;
-            final_best = wave_top16(key, surv[wave], res[wave], lane);
+            // The partitions' results, at most 4 x 16 = 64 keys, one per
+            // lane.  Each list is sorted; with lists 1 and 3 reversed the
+            // lanes hold 16-blocks sorted descending and ascending in turn,
+            // so the merge steps of a bitonic sort (K = 32, 64) finish it.
+            const int p = lane / kTopk, r = lane % kTopk;
+            const int src = (p & 1) ? kTopk - 1 - r : r;
+            uint64_t x = p < waves_per_row ? part_best[row_in_block * waves_per_row + p][src] : 0;
+            x = bitonic_step<32, 16>(x, lane);
+            x = bitonic_step<32, 8>(x, lane);
+            x = bitonic_step<32, 4>(x, lane);
+            x = bitonic_step<32, 2>(x, lane);
+            x = bitonic_step<32, 1>(x, lane);
+            x = bitonic_step<64, 32>(x, lane);
+            x = bitonic_step<64, 16>(x, lane);
+            x = bitonic_step<64, 8>(x, lane);
+            x = bitonic_step<64, 4>(x, lane);
+            x = bitonic_step<64, 2>(x, lane);
+            x = bitonic_step<64, 1>(x, lane);
+            final_best = x;
         }
     }
     if (!live || part != 0)
@@ -266,21 +406,27 @@ hipError_t launch_topk16(const float *scores, int64_t row_stride, int32_t num_ro
                          const int32_t *force_end, const int32_t *append_page, int32_t *out,
                          int64_t out_stride, hipStream_t stream)
 {
-    // Partitions per row: about one pass (256 columns) each, a power of two
-    // up to 16; rows share a work-group of up to 16 waves.
-    const int64_t passes = ((int64_t)width + kPassCols - 1) / kPassCols;
+    // Partitions per row: about one pass (1,024 columns) each, 1, 2 or 4;
+    // rows share a work-group of 4 waves.  Rows of at most 256 columns take
+    // 4 columns per lane.
+    const bool narrow = width <= kNarrowLane * kWave;
+    const int64_t pass_cols = (int64_t)kWideLane * kWave;
+    const int64_t passes = ((int64_t)width + pass_cols - 1) / pass_cols;
     int wpr = 1;
     while (wpr < kMaxWavesPerRow && wpr < passes)
         wpr *= 2;
-    int rows_per_block = 4 / wpr;
-    rows_per_block = rows_per_block < 1 ? 1 : rows_per_block;
-    const int threads = wpr * rows_per_block * kWave;
+    const int rows_per_block = kBlockWaves / wpr;
     const int64_t blocks = ((int64_t)num_rows + rows_per_block - 1) / rows_per_block;
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(topk16_kernel, dim3((uint32_t)blocks), dim3(threads), 0, stream, scores,
-                       row_stride, num_rows, width, valid_len, force_begin, force_end,
-                       append_page, (int32_t)wpr, out, out_stride);
+    if (narrow)
+        hipLaunchKernelGGL(topk16_kernel<kNarrowLane>, dim3((uint32_t)blocks), dim3(kBlockWaves * kWave),
+                           0, stream, scores, row_stride, num_rows, width, valid_len, force_begin,
+                           force_end, append_page, (int32_t)wpr, out, out_stride);
+    else
+        hipLaunchKernelGGL(topk16_kernel<kWideLane>, dim3((uint32_t)blocks), dim3(kBlockWaves * kWave),
+                           0, stream, scores, row_stride, num_rows, width, valid_len, force_begin,
+                           force_end, append_page, (int32_t)wpr, out, out_stride);
     return hipGetLastError();
 }
 
