@@ -19,6 +19,8 @@ bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--pools P]
   python bench.py --profile-pass     # short fixed sequence for rocprofv3 counter runs
+  python bench.py --workload prefill # lightning-indexer prefill step (scores + top-16)
+  python bench.py --workload dequant # NVFP4 gather-dequantize of the decode pages
 """
 
 from __future__ import annotations
@@ -75,7 +77,166 @@ def parse():
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
+    ap.add_argument("--workload", choices=("decode", "prefill", "dequant"), default="decode")
     return ap.parse_args()
+
+
+def timed(torch, stream, fn, n):
+    """Average milliseconds per call of `fn` over `n` back-to-back calls, from
+    two HIP events on the stream the kernels run on."""
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(n):
+        fn(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / n
+
+
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def bench_prefill(args):
+    """Lightning-indexer prefill: 2,048 query tokens x 64 heads against 16,384
+    keys, f32 scores, then the top-16 of every score row."""
+    import torch
+
+    import page_scoring_top_amd as ps
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    d = workloads.big_prefill()
+    T, H = d.q.shape[0], d.q.shape[1]
+    N = d.k.shape[0]
+    q = torch.from_numpy(d.q).to(dev)
+    qs = torch.from_numpy(d.q_scale).to(dev)
+    k = torch.from_numpy(d.k).to(dev)
+    ks = torch.from_numpy(d.k_scale).to(dev)
+    scores = torch.zeros((T, N), dtype=torch.float32, device=dev)
+    out = torch.zeros((T, 16), dtype=torch.int32, device=dev)
+    score_call = ps.prepare(ps.indexer_score_prefill, q, qs, k, ks, scores)
+    topk_call = ps.prepare(ps.topk16_select, scores, N, out)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        score_call()
+        topk_call()
+    torch.cuda.synchronize()
+    K = args.steps
+
+    def step(i):
+        score_call()
+        topk_call()
+
+    ms_per_step = timed(torch, stream, step, K)
+    score_ms = timed(torch, stream, lambda i: score_call(), K)
+    topk_ms = timed(torch, stream, lambda i: topk_call(), K)
+    flops = 2.0 * T * N * H * 128          # the contraction (the epilogue is not counted)
+    achieved = flops / (score_ms * 1e-3) / 1e12
+    result = {
+        "metric": "lightning-indexer prefill TFLOP/s (contraction) + top-16 rows/s",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "e4m3 values as f16, f32 accumulate", "data": "synthetic",
+        "config": {"workload": "lightning-indexer prefill: 2,048 tokens x 64 heads x depth 128 "
+                               "against 16,384 keys, then top-16 of 2,048 rows",
+                   "tokens": T, "heads": H, "keys": N, "depth": 128, "parallelism": "single GPU"},
+        "top16_rows_per_s": round(T / (topk_ms * 1e-3), 1),
+        "kernels_us": {"indexer_score_prefill": round(score_ms * 1e3, 3),
+                       "topk16_select": round(topk_ms * 1e3, 3)},
+        "roofline": {"bound": "mfma", "kernel": "indexer_score_prefill",
+                     "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops_per_launch": flops},
+    }
+    if not args.no_cpu:
+        import oracle
+        t0 = time.perf_counter()
+        n = 0
+        while n < T and time.perf_counter() - t0 < args.cpu_seconds:
+            oracle.score_prefill_rows(d.q, d.q_scale, d.k, d.k_scale, [n])
+            n += 1
+        t_rows = time.perf_counter() - t0
+        cpu_step = t_rows * T / n
+        result["cpu_baseline"] = {
+            "value": round(flops / cpu_step / 1e12, 9), "unit": "TFLOP/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"oracle prefill scores of {n} full rows ({t_rows:.2f} s), scaled to {T} rows; "
+                      f"top-16 not included; step estimate {cpu_step:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
+def bench_dequant(args):
+    """Gather-dequantize of every scored page of the 500K-token decode batch
+    (15,624 pages) into contiguous E4M3 pages, rotating over index-K pools."""
+    import torch
+
+    import page_scoring_top_amd as ps
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    d = workloads.long_decode()
+    R, W = d.num_reqs, d.width
+    P = max(1, args.pools)
+    pools = [torch.from_numpy(d.kv_cache).to(dev)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    for _ in range(1, P):
+        kv = torch.empty_like(pools[0])
+        kv[:, :8192] = torch.randint(0, 256, (kv.shape[0], 8192), generator=gen, device=dev,
+                                     dtype=torch.uint8)
+        kv[:, 8192:] = torch.randint(1, 127, (kv.shape[0], 1024), generator=gen, device=dev,
+                                     dtype=torch.uint8)
+        pools.append(kv)
+    bt = torch.from_numpy(d.block_table[:R]).to(dev)
+    npages = [min(max((int(s) - 1) // 128, 0), W) for s in d.seq_lens[:R]]
+    num_pages = torch.tensor(npages, dtype=torch.int32, device=dev)
+    offs = torch.tensor([sum(npages[:i]) for i in range(R)], dtype=torch.int32, device=dev)
+    total = sum(npages)
+    out = torch.empty((total, 128, 128), dtype=torch.uint8, device=dev)
+    calls = [ps.prepare(ps.nvfp4_index_k_dequant, kv, bt, num_pages, offs, W, out) for kv in pools]
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        calls[i % P]()
+    torch.cuda.synchronize()
+    K = args.steps
+    ms = timed(torch, stream, lambda i: calls[i % P](), K)
+    algo = total * (9216 + 4 + 16384) + R * 8
+    achieved = algo / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "NVFP4 index-K gather-dequantize GB/s (bytes in + out)",
+        "value": round(achieved, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u8 (e4m3 bytes out)", "data": "synthetic",
+        "config": {"workload": "gather-dequantize of the 500K-token decode batch: 4 requests x "
+                               "3,906 NVFP4 pages into contiguous E4M3 pages",
+                   "pages": total, "index_k_pools": P, "parallelism": "single GPU"},
+        "kernels_us": {"nvfp4_index_k_dequant": round(ms * 1e3, 3)},
+        "roofline": {"bound": "hbm", "kernel": "nvfp4_index_k_dequant",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": algo},
+    }
+    if not args.no_cpu:
+        import numpy as np
+        import oracle
+        t0 = time.perf_counter()
+        n = 0
+        ids = d.block_table[0]
+        while n < total and time.perf_counter() - t0 < args.cpu_seconds:
+            oracle.dequant_page(d.kv_cache[ids[n % W]])
+            n += 1
+        t = time.perf_counter() - t0
+        cpu_step = t * total / n
+        result["cpu_baseline"] = {
+            "value": round(algo / cpu_step / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle dequantization of {n} pages ({t:.2f} s), scaled to {total} pages"}
+        del np
+    print(json.dumps(result), flush=True)
 
 
 def main():
@@ -86,13 +247,18 @@ def main():
                           "has no multi-GPU mode", "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
-    import numpy as np
     import torch
+    torch.cuda.set_device(0)
+    if args.workload == "prefill":
+        return bench_prefill(args)
+    if args.workload == "dequant":
+        return bench_dequant(args)
+
+    import numpy as np
 
     import page_scoring_top_amd as ps
     import workloads
 
-    torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     d = workloads.long_decode()
     R, W, qlen = d.num_reqs, d.width, d.qlen
@@ -151,29 +317,16 @@ def main():
         topk_call()
     torch.cuda.synchronize()
 
-    def timed(fn, n):
-        """Average milliseconds per call of `fn` over `n` back-to-back calls,
-        from two HIP events on the stream the kernels run on."""
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record(stream)
-        for i in range(n):
-            fn(i)
-        stop.record(stream)
-        torch.cuda.synchronize()
-        return start.elapsed_time(stop) / n
-
     def step(i):
         score_calls[i % P]()
         topk_call()
 
     K = args.steps
     # The timed region: K whole steps back to back.
-    ms_per_step = timed(step, K)
+    ms_per_step = timed(torch, stream, step, K)
     # Each kernel's average launch duration, from runs of that kernel alone.
-    score_avg = timed(lambda i: score_calls[i % P](), K)
-    topk_avg = timed(lambda i: topk_call(), K)
+    score_avg = timed(torch, stream, lambda i: score_calls[i % P](), K)
+    topk_avg = timed(torch, stream, lambda i: topk_call(), K)
 
     value = kbytes / (ms_per_step * 1e-3) / 1e9
     achieved = algo_bytes / (score_avg * 1e-3) / 1e9

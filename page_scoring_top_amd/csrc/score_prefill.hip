@@ -105,16 +105,19 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
                                                                 acc, 0, 0, 0);
                 }
                 // Lane holds rows 8*(i/4) + 4*half + i%4 (i = 0..15) of its key column.
+                // The sum runs on x + |x| = 2 relu(x), one add and one fma per
+                // element; scaling by 2 commutes with every rounding, so half
+                // of it at the end equals the sum of relu(x) * q_scale.
                 const float *qs = qsl + (size_t)tt * hp + 32 * ht + 4 * half;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float x = acc[i];
-                    sum = fmaf((x + fabsf(x)) * 0.5f, qs[8 * (i / 4) + (i % 4)], sum);
+                    sum = fmaf(x + fabsf(x), qs[8 * (i / 4) + (i % 4)], sum);
                 }
             }
             sum += __shfl_xor(sum, 32);
             if (half == 0 && key_ok)
-                scores[(t0 + tt) * ld + n] = ks * sum;
+                scores[(t0 + tt) * ld + n] = ks * (0.5f * sum);
         }
     }
 }
