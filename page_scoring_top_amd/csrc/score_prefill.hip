@@ -122,6 +122,172 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Heads <= 64: query rows in registers, keys streamed through LDS.
+//
+// A wave owns two tokens and keeps their query rows as MFMA A operands in
+// VGPRs for the whole key range (two 32-head tiles x eight 16-deep K steps x
+// two tokens = 128 VGPRs), so each B operand read from LDS feeds four MFMAs.
+// The work-group's four waves convert the keys to f16 together, 128 keys at
+// a time, into one of two LDS buffers while they compute on the other; one
+// barrier per 128 keys.  A work-group covers 8 tokens and a contiguous range
+// of keys (the key range is split so the grid fills the chip).  Rows of the key buffer are padded to 272 bytes so
+// the 32 keys a B read touches fall on distinct banks.
+// ---------------------------------------------------------------------------
+constexpr int kTokPerWave = 2;
+constexpr int kTokPerGroup = kWavesPerBlock * kTokPerWave;   // 8
+constexpr int kChunkKeys = 128;
+constexpr int kKeyRowBytes = kRowHalves * 2;                  // 272
+constexpr int kSmallHeads = 64;
+
+__global__ __launch_bounds__(256, 2) void score_prefill_h64_kernel(
+    const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
+    const uint8_t *__restrict__ k, const float *__restrict__ k_scale, int32_t T, int32_t H,
+    int32_t N, int32_t keys_per_group, float *__restrict__ scores, int64_t ld)
+{
+    __shared__ __align__(16) uint8_t kbuf[2][kChunkKeys * kKeyRowBytes];
+    __shared__ __align__(16) float qs_lds[kTokPerGroup][kSmallHeads];
+    __shared__ float ks_lds[2][kChunkKeys];
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    const int64_t tg = (int64_t)blockIdx.x * kTokPerGroup;
+    const int kb = blockIdx.y * keys_per_group;
+    const int ke = kb + keys_per_group < N ? kb + keys_per_group : N;
+
+    // Query rows of this wave's two tokens as f16 A operands: head 32 ht +
+    // col, depth 16 s + 8 half .. +8 (zero past H or T).
+    u32x4 a[kTokPerWave][2][8];
+#pragma unroll
+    for (int tk = 0; tk < kTokPerWave; ++tk) {
+        const int64_t t = tg + wave * kTokPerWave + tk;
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+            const int h = 32 * ht + col;
+            const bool ok = t < T && h < H;
+            const uint8_t *src = q + ((ok ? t : 0) * H + (ok ? h : 0)) * kDepth + 8 * half;
+#pragma unroll
+            for (int st = 0; st < 8; ++st) {
+                uint2 b = make_uint2(0u, 0u);
+                if (ok)
+                    b = *reinterpret_cast<const uint2 *>(src + 16 * st);
+                a[tk][ht][st] = f16_of_8_bytes(b.x, b.y);
+            }
+        }
+    }
+    for (int i = tid; i < kTokPerGroup * kSmallHeads; i += blockDim.x) {
+        const int tt = i / kSmallHeads, h = i % kSmallHeads;
+        const int64_t t = tg + tt;
+        qs_lds[tt][h] = (t < T && h < H) ? q_scale[t * H + h] : 0.0f;
+    }
+
+    // Key conversion: thread -> key tid / 2 of the chunk, depth half tid % 2
+    // (64 elements: four 16-byte loads, 32 conversions, eight 16-byte
+    // stores).  The loads of chunk i+1 are issued before chunk i is computed
+    // and converted after it, so their latency hides behind the MFMAs.
+    const int ck = tid >> 1, cd = (tid & 1) * 64;
+    struct Raw {
+        u32x4 v[4];
+        float ks;
+    };
+    auto load_chunk = [&](int chunk_base, Raw &r) {
+        const int n = chunk_base + ck;
+        const bool ok = n < ke;
+        const int64_t nn = ok ? n : kb;   // a valid key; its values are not used
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            r.v[i] = *reinterpret_cast<const u32x4 *>(k + nn * kDepth + cd + 16 * i);
+        r.ks = k_scale[nn];
+        if (!ok) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                r.v[i] = u32x4{0u, 0u, 0u, 0u};
+            r.ks = 0.0f;
+        }
+    };
+    auto store_chunk = [&](const Raw &r, int buf) {
+        uint8_t *dst = &kbuf[buf][ck * kKeyRowBytes + cd * 2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *reinterpret_cast<u32x4 *>(dst + 32 * i) = f16_of_8_bytes(r.v[i][0], r.v[i][1]);
+            *reinterpret_cast<u32x4 *>(dst + 32 * i + 16) = f16_of_8_bytes(r.v[i][2], r.v[i][3]);
+        }
+        if ((tid & 1) == 0)
+            ks_lds[buf][ck] = r.ks;
+    };
+
+    if (kb < ke) {
+        Raw r0;
+        load_chunk(kb, r0);
+        store_chunk(r0, 0);
+    }
+    __syncthreads();
+
+    int buf = 0;
+    for (int cb = kb; cb < ke; cb += kChunkKeys, buf ^= 1) {
+        const bool has_next = cb + kChunkKeys < ke;
+        Raw nxt;
+        if (has_next)
+            load_chunk(cb + kChunkKeys, nxt);
+
+        const uint8_t *kt_base = &kbuf[buf][0];
+#pragma unroll 1
+        for (int kt = 0; kt < kChunkKeys / 32; ++kt) {
+            const int n = cb + kt * 32 + col;
+            if (cb + kt * 32 >= ke)
+                break;
+            v16f acc[kTokPerWave][2];
+#pragma unroll
+            for (int tk = 0; tk < kTokPerWave; ++tk)
+#pragma unroll
+                for (int ht = 0; ht < 2; ++ht)
+                    acc[tk][ht] = v16f{};
+            const uint8_t *brow = kt_base + (kt * 32 + col) * kKeyRowBytes + 16 * half;
+#pragma unroll
+            for (int st = 0; st < 8; ++st) {
+                const v8h b = __builtin_bit_cast(v8h, *reinterpret_cast<const u32x4 *>(brow + 32 * st));
+#pragma unroll
+                for (int tk = 0; tk < kTokPerWave; ++tk)
+#pragma unroll
+                    for (int ht = 0; ht < 2; ++ht)
+                        acc[tk][ht] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            __builtin_bit_cast(v8h, a[tk][ht][st]), b, acc[tk][ht], 0, 0, 0);
+            }
+            const float ks = ks_lds[buf][kt * 32 + col];
+#pragma unroll
+            for (int tk = 0; tk < kTokPerWave; ++tk) {
+                const int tt = wave * kTokPerWave + tk;
+                float sum = 0.0f;
+#pragma unroll
+                for (int ht = 0; ht < 2; ++ht) {
+                    // Lane holds heads 32 ht + 8 (i/4) + 4 half + i%4, i = 0..15.
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const float4 qs4 = *reinterpret_cast<const float4 *>(
+                            &qs_lds[tt][32 * ht + 8 * g + 4 * half]);
+                        const float qv[4] = {qs4.x, qs4.y, qs4.z, qs4.w};
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float x = acc[tk][ht][4 * g + r];
+                            sum = fmaf(x + fabsf(x), qv[r], sum);
+                        }
+                    }
+                }
+                sum += __shfl_xor(sum, 32);
+                const int64_t t = tg + tt;
+                if (half == 0 && n < ke && t < T)
+                    scores[t * ld + n] = ks * (0.5f * sum);
+            }
+        }
+        // The other buffer's readers finished before the previous barrier.
+        if (has_next)
+            store_chunk(nxt, buf ^ 1);
+        __syncthreads();
+    }
+}
+
 }  // namespace
 
 static_assert(kPrefillMaxHeads * ((kRowHalves * 2) + 4) <= kLdsBytes,
@@ -131,6 +297,22 @@ hipError_t launch_score_prefill(const uint8_t *q, const float *q_scale, const ui
                                 const float *k_scale, int32_t T, int32_t H, int32_t N,
                                 float *scores, int64_t ld, hipStream_t stream)
 {
+    if (H <= kSmallHeads) {
+        // Token groups of 8; the keys are split so that the grid holds about
+        // two work-groups per compute unit, in whole chunks of 128 keys.
+        const int64_t groups = ((int64_t)T + kTokPerGroup - 1) / kTokPerGroup;
+        if (groups > 0x7FFFFFFF)
+            return hipErrorInvalidValue;
+        const int64_t chunks = ((int64_t)N + kChunkKeys - 1) / kChunkKeys;
+        int64_t splits = (512 + groups - 1) / groups;
+        splits = splits < 1 ? 1 : (splits > chunks ? chunks : splits);
+        const int64_t keys_per_group = ((chunks + splits - 1) / splits) * kChunkKeys;
+        splits = ((int64_t)N + keys_per_group - 1) / keys_per_group;
+        hipLaunchKernelGGL(score_prefill_h64_kernel, dim3((uint32_t)groups, (uint32_t)splits),
+                           dim3(256), 0, stream, q, q_scale, k, k_scale, T, H, N,
+                           (int32_t)keys_per_group, scores, ld);
+        return hipGetLastError();
+    }
     const int hp = (H + 31) & ~31;
     const size_t per_token = (size_t)hp * (kRowHalves * 2 + 4);
     int tb = (int)(kLdsBytes / per_token);
