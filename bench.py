@@ -38,13 +38,13 @@ sys.path.insert(0, ROOT)
 METRIC = "index-K GB/s scored (frac of HBM peak) + top-16 rows/s, 500K-token decode"
 HBM_PEAK_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "score_decode_long_counters.txt")
-SCORE_SOURCES = ["score_decode.hip", "device_common.hpp", "nvfp4_lut.hpp"]
+SCORE_SOURCES = ["csrc/score_decode.hip", "csrc/device_common.hpp", "csrc/nvfp4_lut.hpp", "build.py"]
 
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in SCORE_SOURCES:
-        with open(os.path.join(ROOT, "page_scoring_top_amd", "csrc", f), "rb") as fh:
+        with open(os.path.join(ROOT, "page_scoring_top_amd", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 

@@ -76,7 +76,8 @@ extern "C" {
  *   out_pages         pages in out.
  * Pages whose id is outside [0, num_blocks), or whose output page is outside
  * [0, out_pages), are skipped (nothing read or written for them).
- * num_reqs == 0 or max_num_pages == 0 returns PAGESCORE_OK with no launch.
+ * num_reqs == 0 or max_num_pages == 0 returns PAGESCORE_OK with no launch;
+ * num_reqs above 65,535 is PAGESCORE_EINVAL (one grid row per request).
  */
 int nvfp4_index_k_dequant(const uint8_t *kv_cache, int64_t page_stride_bytes,
                           int64_t num_blocks, const int32_t *block_table,

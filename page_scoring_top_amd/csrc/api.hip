@@ -55,7 +55,7 @@ int nvfp4_index_k_dequant(const uint8_t *kv_cache, int64_t page_stride_bytes, in
                           const int32_t *page_offsets, int32_t num_reqs, int32_t max_num_pages,
                           uint8_t *out, int64_t out_pages, void *stream)
 {
-    if (num_reqs < 0 || max_num_pages < 0)
+    if (num_reqs < 0 || num_reqs > pagescore::kDequantMaxReqs || max_num_pages < 0)
         return PAGESCORE_EINVAL;
     if (num_reqs == 0 || max_num_pages == 0)
         return PAGESCORE_OK;

@@ -4,13 +4,14 @@
 // minimax_m3_gather_nvfp4_index_k_fp8 (which pages go where) and the module
 // description (page format; element = e4m3_rn_satfinite(e2m1 * scale)).
 //
-// One wave per output page.  Per round i (0..7) the wave reads 1 KiB of codes
-// (16 tokens x 64 B, one 16-byte load per lane, contiguous across the wave)
-// and 128 B of scales (two bytes per lane), and writes 2 KiB of E4M3 output
-// (two 16-byte stores per lane, contiguous).  Lane l works on token 16i + l/4,
-// elements 32*(l%4) .. 32*(l%4) + 31 (block-scale groups 2*(l%4) and +1).
-// The page's 9 KiB in and 16 KiB out are each touched once: the kernel is
-// bound by HBM at 25,600 algorithmic bytes per page.
+// A wave dequantizes a run of pages, one at a time.  Per round i (0..7) of a
+// page it reads 1 KiB of codes (16 tokens x 64 B, one 16-byte load per lane,
+// contiguous across the wave) and 128 B of scales (two bytes per lane), and
+// writes 2 KiB of E4M3 output (two 16-byte stores per lane, contiguous).
+// Lane l works on token 16i + l/4, elements 32*(l%4) .. 32*(l%4) + 31
+// (block-scale groups 2*(l%4) and +1).  The page's 9 KiB in and 16 KiB out
+// are each touched once: the kernel is bound by HBM at 25,604 algorithmic
+// bytes per page (with its block-table entry).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -18,51 +19,57 @@ namespace pagescore {
 
 namespace {
 
-constexpr int kPagesPerBlock = 4;  // one wave per page
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void nvfp4_dequant_kernel(
-    const uint8_t *__restrict__ kv, int64_t page_stride, int64_t num_blocks,
-    const int32_t *__restrict__ block_table, int64_t bt_stride,
-    const int32_t *__restrict__ num_pages, const int32_t *__restrict__ page_offsets,
-    int32_t max_num_pages, int32_t blocks_per_req, uint8_t *__restrict__ out, int64_t out_pages)
+constexpr int kWavesPerBlock = 4;
+constexpr int kStreamLoad = 2;    // buffer cache policy: nontemporal (read once)
+
+// A descriptor covering one page; with no records, loads through it return
+// zeros without touching memory, so a wave issues the same loads for every
+// page of its run, whether the page exists or not.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t *page, bool live)
 {
-    __shared__ uint64_t lut[256];
-    load_lut_to_lds(lut);
-    __syncthreads();
+    const uint64_t a = reinterpret_cast<uintptr_t>(page);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const int records = __builtin_amdgcn_readfirstlane(live ? kPageBytes : 0);
+    return __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), (short)0, records, 0x00020000);
+}
 
-    const int wave = threadIdx.x / kWave;
-    const int lane = threadIdx.x % kWave;
-    const int r = blockIdx.x / blocks_per_req;
-    const int j = (blockIdx.x % blocks_per_req) * kPagesPerBlock + wave;
-    int n = num_pages[r];
-    n = n < max_num_pages ? n : max_num_pages;
-    if (j >= n)
-        return;
-    const int64_t pid = block_table[(int64_t)r * bt_stride + j];
-    const int64_t opage = (int64_t)page_offsets[r] + j;
-    if (pid < 0 || pid >= num_blocks || opage < 0 || opage >= out_pages)
-        return;
-    const uint8_t *src = kv + pid * page_stride;
-    uint8_t *dst = out + opage * (kPageTokens * kDepth);
-
-    const int chunk = lane & 3;      // 32-element chunk of the token
-    const int tok_in_round = lane >> 2;
-
-    uint4 codes[8];
+// One page in registers: round i (tokens 16 i .. 16 i + 15) is 1 KiB of
+// codes, 16 bytes per lane, and the round's 128 scale bytes, 2 per lane
+// (lane l: token 16 i + l / 4, groups 2 (l % 4) and 2 (l % 4) + 1).
+struct PageIn {
+    u32x4 codes[8];
     uint32_t sc[8];
+};
+
+__device__ __forceinline__ void load_page(PageIn &p, __amdgpu_buffer_rsrc_t src, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        p.codes[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(src, 1024 * i + 16 * lane, 0, kStreamLoad));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        p.sc[i] = __builtin_amdgcn_raw_buffer_load_b16(src, kCodeBytes + 128 * i + 2 * lane, 0,
+                                                       kStreamLoad);
+}
+
+// Dequantize a page held in registers and write the 16 KiB of E4M3 out:
+// per round, two 16-byte stores per lane (32 output bytes: the lane's 32
+// elements of its token), contiguous across the wave.  Plain stores: the
+// nontemporal form measured about a quarter slower here.
+__device__ __forceinline__ void store_page(const PageIn &p, const uint64_t *lut, uint8_t *dst, int lane)
+{
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        codes[i] = *reinterpret_cast<const uint4 *>(src + 1024 * i + 16 * lane);
-        sc[i] = *reinterpret_cast<const uint16_t *>(src + kCodeBytes + (16 * i + tok_in_round) * 8 +
-                                                    2 * chunk);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t w[4] = {codes[i].x, codes[i].y, codes[i].z, codes[i].w};
+        const uint32_t w[4] = {p.codes[i][0], p.codes[i][1], p.codes[i][2], p.codes[i][3]};
         uint32_t o[8];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            const uint32_t s = (sc[i] >> (8 * hh)) & 0xFFu;
+            const uint32_t s = (p.sc[i] >> (8 * hh)) & 0xFFu;
             const uint64_t t = lut[s];
             const uint32_t flip = scale_sign_flip(s);
             const bool nan = scale_is_nan(s);
@@ -79,9 +86,68 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(
                 o[4 * hh + 2 * k + 1] = b;
             }
         }
-        uint4 *d = reinterpret_cast<uint4 *>(dst + 2048 * i + 32 * lane);
-        d[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        d[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        u32x4 *d = reinterpret_cast<u32x4 *>(dst + 2048 * i + 32 * lane);
+        d[0] = u32x4{o[0], o[1], o[2], o[3]};
+        d[1] = u32x4{o[4], o[5], o[6], o[7]};
+    }
+}
+
+// Work-group (x, r) covers request r; each wave owns a run of `run` logical
+// pages.  The run's page ids, the request's page count and output offset
+// and the table are requested at once; the first page follows as soon as
+// the ids are in, and each page's successor is in flight while it is
+// dequantized and stored.
+__global__ __launch_bounds__(256) void nvfp4_dequant_kernel(
+    const uint8_t *__restrict__ kv, int64_t page_stride, int64_t num_blocks,
+    const int32_t *__restrict__ block_table, int64_t bt_stride,
+    const int32_t *__restrict__ num_pages, const int32_t *__restrict__ page_offsets,
+    int32_t max_num_pages, int32_t run, uint8_t *__restrict__ out, int64_t out_pages)
+{
+    __shared__ uint64_t lut[256];
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int r = blockIdx.y;
+    const int j0 = (blockIdx.x * kWavesPerBlock + wave) * run;
+
+    int n = num_pages[r];
+    const int64_t off = page_offsets[r];
+    int32_t id_lane = -1;
+    if (lane < run && j0 + lane < max_num_pages)
+        id_lane = block_table[(int64_t)r * bt_stride + j0 + lane];
+    const uint64_t lut_entry = kNvfp4Lut.entry[tid];
+    n = n < max_num_pages ? n : max_num_pages;
+    const int j1 = j0 + run < n ? j0 + run : n;
+
+    // Page j is dequantized when its id is in range and its output page is
+    // inside `out`; otherwise nothing is read or written for it.
+    auto page_src = [&](int j, bool &ok) -> __amdgpu_buffer_rsrc_t {
+        const int64_t id = __builtin_amdgcn_readlane(id_lane, j - j0);
+        const int64_t opage = off + j;
+        ok = j < j1 && id >= 0 && id < num_blocks && opage >= 0 && opage < out_pages;
+        return page_rsrc(kv + (ok ? id : 0) * page_stride, ok);
+    };
+    PageIn pa, pb;
+    bool ok_a = false, ok_b = false;
+    if (j0 < j1)
+        load_page(pa, page_src(j0, ok_a), lane);
+    lut[tid] = lut_entry;
+    __syncthreads();
+    if (j0 >= j1)
+        return;
+
+    int j = j0;
+    auto step = [&](const PageIn &cur, bool cur_ok, PageIn &nxt, bool &nxt_ok) -> bool {
+        load_page(nxt, page_src(j + 1 < j1 ? j + 1 : j1, nxt_ok), lane);
+        if (cur_ok)
+            store_page(cur, lut, out + (off + j) * (kPageTokens * kDepth), lane);
+        return ++j < j1;
+    };
+    for (;;) {
+        if (!step(pa, ok_a, pb, ok_b))
+            break;
+        if (!step(pb, ok_b, pa, ok_a))
+            break;
     }
 }
 
@@ -93,13 +159,17 @@ hipError_t launch_nvfp4_dequant(const uint8_t *kv, int64_t page_stride, int64_t 
                                 int32_t num_reqs, int32_t max_num_pages, uint8_t *out,
                                 int64_t out_pages, hipStream_t stream)
 {
-    const int32_t blocks_per_req = (max_num_pages + kPagesPerBlock - 1) / kPagesPerBlock;
-    const int64_t grid = (int64_t)blocks_per_req * num_reqs;
-    if (grid > 0x7FFFFFFF)
+    // Pages per wave: the batch's upper bound spread over about 16 waves per
+    // compute unit, 1..8 (a run's ids fit one wave's lanes).
+    const int64_t max_pages = (int64_t)num_reqs * max_num_pages;
+    int64_t run = (max_pages + 256 * 16 - 1) / (256 * 16);
+    run = run < 1 ? 1 : (run > 8 ? 8 : run);
+    const int64_t gx = ((int64_t)max_num_pages + run * kWavesPerBlock - 1) / (run * kWavesPerBlock);
+    if (gx > 0x7FFFFFFF || num_reqs > 65535)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, kv,
-                       page_stride, num_blocks, block_table, bt_stride, num_pages, page_offsets,
-                       max_num_pages, blocks_per_req, out, out_pages);
+    hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3((uint32_t)gx, (uint32_t)num_reqs), dim3(256), 0,
+                       stream, kv, page_stride, num_blocks, block_table, bt_stride, num_pages,
+                       page_offsets, max_num_pages, (int32_t)run, out, out_pages);
     return hipGetLastError();
 }
 

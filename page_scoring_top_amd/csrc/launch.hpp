@@ -6,8 +6,10 @@
 
 namespace pagescore {
 
-// Requests per indexer_score_decode call: one grid row per request.
+// Requests per indexer_score_decode or nvfp4_index_k_dequant call: one grid
+// row per request.
 constexpr int32_t kDecodeMaxReqs = 65535;
+constexpr int32_t kDequantMaxReqs = 65535;
 
 // Heads per indexer_score_prefill call: a work-group keeps one token's query
 // rows (heads rounded up to 32) as f16 in LDS.

@@ -65,6 +65,7 @@ def test_dequant_host_checks(lib):
     assert _dequant(lib, R=0) == 0                       # nothing to do: no launch
     assert _dequant(lib, maxp=0) == 0
     assert _dequant(lib, R=-1) == EINVAL
+    assert _dequant(lib, R=65536) == EINVAL              # beyond the per-call request limit
     assert _dequant(lib, kv=None) == EINVAL
     assert _dequant(lib, kv=ODD) == EINVAL               # misaligned
     assert _dequant(lib, stride=9215) == EINVAL
