@@ -129,8 +129,7 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(
     };
     PageIn pa, pb;
     bool ok_a = false, ok_b = false;
-    if (j0 < j1)
-        load_page(pa, page_src(j0, ok_a), lane);
+    load_page(pa, page_src(j0, ok_a), lane);   // unconditional: empty descriptor for an empty run
     lut[tid] = lut_entry;
     __syncthreads();
     if (j0 >= j1)

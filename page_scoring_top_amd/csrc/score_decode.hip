@@ -343,10 +343,13 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
         ok = j < j1 && id >= 0 && id < num_blocks;
         return page_rsrc(kv + (ok ? id : 0) * page_stride, ok);
     };
+    // The first page is requested without a branch (an empty run gets an
+    // empty descriptor): after a conditional load the compiler could not
+    // count the loads in flight and would wait for the page before the
+    // query conversion below.
     PageRegs pa, pb;
     bool ok_a = false, ok_b = false;
-    if (j0 < j1)
-        fetch_page(pa, page_src(j0, ok_a), lane, m, g);
+    fetch_page(pa, page_src(j0, ok_a), lane, m, g);
 
     lut[tid] = lut_entry_g;
     RequestRegs rq;
@@ -363,6 +366,10 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
     // from `cur`.
     auto step = [&](const PageRegs &cur, bool cur_ok, PageRegs &nxt, bool &nxt_ok) -> bool {
         fetch_page(nxt, page_src(j + 1 < j1 ? j + 1 : j1, nxt_ok), lane, m, g);
+        // Keep the next page's loads ahead of everything that reads this
+        // page: scheduled after the scale unpacking they would wait for this
+        // page's last load, leaving nothing in flight.
+        __builtin_amdgcn_sched_barrier(0);
         if (cur_ok) {
             uint32_t sc[8];
             unpack_scales(cur, stage, lane, m, g, sc);

@@ -147,11 +147,13 @@ __device__ __forceinline__ T bitonic_step(T x, int lane)
     return ((y > x) == keep_max) ? y : x;
 }
 
-// Descending sort of one value per lane across the wave: lane 0 ends with
-// the largest.
-template <typename T>
+// Descending sort of one value per lane over the first N lanes (16, 32 or
+// 64) of the wave: lane 0 ends with the largest.  The lanes past N end in
+// some other order.
+template <int N, typename T>
 __device__ __forceinline__ T wave_sort_desc(T x, int lane)
 {
+    static_assert(N == 16 || N == 32 || N == 64, "sort width");
     x = bitonic_step<2, 1>(x, lane);
     x = bitonic_step<4, 2>(x, lane);
     x = bitonic_step<4, 1>(x, lane);
@@ -162,17 +164,21 @@ __device__ __forceinline__ T wave_sort_desc(T x, int lane)
     x = bitonic_step<16, 4>(x, lane);
     x = bitonic_step<16, 2>(x, lane);
     x = bitonic_step<16, 1>(x, lane);
-    x = bitonic_step<32, 16>(x, lane);
-    x = bitonic_step<32, 8>(x, lane);
-    x = bitonic_step<32, 4>(x, lane);
-    x = bitonic_step<32, 2>(x, lane);
-    x = bitonic_step<32, 1>(x, lane);
-    x = bitonic_step<64, 32>(x, lane);
-    x = bitonic_step<64, 16>(x, lane);
-    x = bitonic_step<64, 8>(x, lane);
-    x = bitonic_step<64, 4>(x, lane);
-    x = bitonic_step<64, 2>(x, lane);
-    x = bitonic_step<64, 1>(x, lane);
+    if constexpr (N >= 32) {
+        x = bitonic_step<32, 16>(x, lane);
+        x = bitonic_step<32, 8>(x, lane);
+        x = bitonic_step<32, 4>(x, lane);
+        x = bitonic_step<32, 2>(x, lane);
+        x = bitonic_step<32, 1>(x, lane);
+    }
+    if constexpr (N == 64) {
+        x = bitonic_step<64, 32>(x, lane);
+        x = bitonic_step<64, 16>(x, lane);
+        x = bitonic_step<64, 8>(x, lane);
+        x = bitonic_step<64, 4>(x, lane);
+        x = bitonic_step<64, 2>(x, lane);
+        x = bitonic_step<64, 1>(x, lane);
+    }
     return x;
 }
 
@@ -248,7 +254,7 @@ __device__ __forceinline__ uint64_t wave_top16(const Candidates<N> &c, uint64_t 
 #pragma unroll
     for (int i = 0; i < N; ++i)
         lmax = c.hi[i] > lmax ? c.hi[i] : lmax;
-    uint32_t t = __builtin_amdgcn_readlane(wave_sort_desc(lmax, lane), kTopk - 1);
+    uint32_t t = __builtin_amdgcn_readlane(wave_sort_desc<64>(lmax, lane), kTopk - 1);
     t = t > 0 ? t : 1;   // real keys only
 
     // Survivors: keys whose high word reaches t.
@@ -279,7 +285,11 @@ __device__ __forceinline__ uint64_t wave_top16(const Candidates<N> &c, uint64_t 
     wave_lds_sync();
     const uint64_t mine = lane < total ? surv[lane] : 0;
     wave_lds_sync();   // the scratch may be rewritten by the caller's next selection
-    const uint64_t sorted = wave_sort_desc(mine, lane);
+    // The survivors sit in lanes 0 .. total-1 (usually about 20): sort only
+    // as many lanes as needed.
+    const uint64_t sorted = total <= 16   ? wave_sort_desc<16>(mine, lane)
+                            : total <= 32 ? wave_sort_desc<32>(mine, lane)
+                                          : wave_sort_desc<64>(mine, lane);
     return lane < kTopk ? sorted : 0;
 }
 

@@ -22,7 +22,10 @@ def gpu_prefill(p: workloads.PrefillInputs, ld=None):
 
 
 @pytest.mark.parametrize("T,H,N", [(1, 1, 1), (3, 1, 33), (5, 3, 64), (7, 32, 100), (9, 33, 31),
-                                   (17, 64, 257), (4, 65, 130)])
+                                   (17, 64, 257), (4, 65, 130),
+                                   # many 128-key chunks, a ragged last chunk and token
+                                   # group, key ranges split over several work-groups
+                                   (13, 48, 1000), (2, 64, 5000), (8, 64, 128), (9, 1, 129)])
 def test_small_shapes_full(T, H, N):
     p = workloads.prefill_inputs("small", T * 1000 + H * 10 + N, T, H, N)
     announce(f"prefill T={T} H={H} N={N}")
