@@ -66,13 +66,4 @@ __device__ __forceinline__ bool scale_is_nan(uint32_t scale_byte)
     return (scale_byte & 0x7Fu) == 0x7Fu;
 }
 
-// Copy the dequantization table into LDS; every thread of the block must call.
-__device__ __forceinline__ void load_lut_to_lds(uint64_t *lds_lut)
-{
-    for (int i = threadIdx.x; i < 256; i += blockDim.x)
-        lds_lut[i] = kNvfp4Lut.entry[i];
-}
-
-__device__ __forceinline__ int lane_id() { return __lane_id(); }
-
 }  // namespace pagescore

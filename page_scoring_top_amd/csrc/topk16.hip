@@ -28,10 +28,11 @@
 // (DPP row and quad moves and the permlane swaps; no LDS) gives t, the 16th
 // largest; (3) every key whose high word reaches t survives -- the 16 lanes
 // whose maxima reach t hold 16 distinct keys no smaller than any key below t,
-// so the best 16 are among the survivors; (4) the survivors are compacted one
-// per lane through LDS (ballot prefix counts) and sorted by a second bitonic
-// sort on the full keys.  When more than 64 keys survive (ties in the score),
-// the exact 16th key is found by a 64-bit bisection over all the keys
+// so the best 16 are among the survivors; (4) the survivors are placed one per
+// lane through LDS (each lane counts its own, a DPP prefix sum gives the
+// places) and sorted by a second bitonic sort on the full keys, over only as
+// many lanes as they occupy.  When more than 64 keys survive (ties in the
+// score), the exact 16th key is found by a 64-bit bisection over all the keys
 // instead, and exactly 16 survive.
 //
 // In a pass, a new key whose high word is below that of the wave's current

@@ -60,11 +60,12 @@ def test_nan_inputs_propagate():
 
 def test_big_config_sampled_rows():
     """2,048 tokens x 64 heads x 16,384 keys in the benchmark's launch
-    configuration; two full rows against the oracle."""
+    configuration; full rows of first, middle and last tokens of work-groups
+    against the oracle."""
     p = workloads.big_prefill()
     announce("prefill 2048 x 64 x 16384")
     got = gpu_prefill(p)
-    rows = [0, 2047]
+    rows = [0, 7, 8, 1029, 2047]
     want = oracle.score_prefill_rows(p.q, p.q_scale, p.k, p.k_scale, rows)
     assert_scores_close(got[rows], want, "big prefill")
     assert np.isfinite(got).all()
