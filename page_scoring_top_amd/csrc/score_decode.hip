@@ -33,21 +33,24 @@
 //
 // Each output lane of a 16x16 tile holds 4 tokens of one query row, so the
 // page maximum is a running per-lane max over the 8 tiles, then 2 cross-lane
-// steps.  On gfx950 the VALU and MFMA work of a SIMD largely serialize
-// (measured), so the per-page cost is their sum: the dequantization keeps to
-// 12 VALU operations per 8 elements on the common path, the MFMA results stay
-// in VGPRs, and pages whose scale bytes are all in 0x00..0x7E (no negative or
-// NaN scale) skip the sign-flip and NaN bookkeeping.
+// steps.  With the 16-cycle MFMA a wave hides only about one VALU instruction
+// behind each MFMA (measured), so the per-page cost is close to the sum of
+// both: the dequantization keeps to 12 VALU operations per 8 elements, and
+// the MFMA results stay in VGPRs.  The table is signed (a negative scale's
+// entry carries the sign bit and the code's sign is XOR-ed in), so negative
+// scales need no extra work and every page takes the same path.
 //
 // Scheduling: work-group (x, b) covers request b; each of its waves owns a run
 // of `chunk` consecutive pages (chosen on the host from the batch size).  A
 // wave issues its first loads -- the request's length, the run's page ids and
 // the query rows -- all at once, so a single memory round trip precedes the
-// first page fetch; then it scores the run with two page buffers in turn, the
-// next page's 9 KiB in flight while the current one is scored (past the run's
-// end the loads go through an empty descriptor and cost nothing).  Runs past a
-// request's last page exit at once, and the hardware dispatcher back-fills the
-// compute units, which balances ragged batches.
+// first page fetch.  Then it scores the run from one set of page registers
+// that is refilled as it is consumed: the next page's scale block as soon as
+// this page's is staged, and the next page's codes of each tile right after
+// the tile is scored, so every load is issued one page-time before its use
+// (past the run's end the loads go through an empty descriptor and cost
+// nothing).  Runs past a request's last page exit at once, and the hardware
+// dispatcher back-fills the compute units, which balances ragged batches.
 //
 // NaN: the MFMA's NaN handling is not relied on.  A NaN scale byte makes every
 // dot of its token NaN, so it marks the whole page NaN; a NaN byte in a query
@@ -71,8 +74,8 @@ struct PageRegs {
     u32x4 scales;     // bytes 16*lane .. 16*lane+15 of the page's 1 KiB of scales
 };
 
-// One page: eight 16-byte code loads per lane (1 KiB per wave each) and one
-// coalesced 16-byte load per lane of the scale block, as buffer loads against
+// One page: one coalesced 16-byte load per lane of the scale block and eight
+// 16-byte code loads per lane (1 KiB per wave each), as buffer loads against
 // a descriptor that covers only this page.  A descriptor with no records
 // makes every load return zeros without touching memory, so a wave issues
 // the same loads for every page, whether it exists or not.
@@ -91,14 +94,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t *page,
         reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), (short)0, records, 0x00020000);
 }
 
+// The scale block first, as the page loop refills it: the first page's loads
+// then stand in the same order as every later page's, and the compiler can
+// wait for each load by the same count (anything else merges to a full wait
+// at the loop head).
 __device__ __forceinline__ void fetch_page(PageRegs &p, __amdgpu_buffer_rsrc_t src, int lane, int m,
                                            int g)
 {
+    p.scales = __builtin_amdgcn_raw_buffer_load_b128(src, kCodeBytes + 16 * lane, 0, kStreamLoad);
 #pragma unroll
     for (int t = 0; t < 8; ++t)
         p.codes[t] = __builtin_amdgcn_raw_buffer_load_b128(src, (16 * t + m) * 64 + 16 * g, 0,
                                                            kStreamLoad);
-    p.scales = __builtin_amdgcn_raw_buffer_load_b128(src, kCodeBytes + 16 * lane, 0, kStreamLoad);
 }
 
 // The 2 scale bytes of tile t for this lane (token 16*t + m, groups 2g and
@@ -219,15 +226,27 @@ __device__ __forceinline__ void finish_request(RequestRegs &rq, const RequestRaw
 // Score one page for the request's 32 rows: the per-lane maxima r0 (row m)
 // and r1 (row 16+m) of the raw dot products, and whether a NaN scale byte
 // makes the whole page NaN.
-template <bool kGeneral>
-__device__ __forceinline__ void score_page(const PageRegs &p, const uint32_t sc[8],
-                                           const uint64_t *lut, const RequestRegs &rq, float &r0,
-                                           float &r1, bool &page_nan)
+// Dequantize the 8 E2M1 codes of one word against a signed table entry
+// (byte c = E4M3 of code magnitude c times the scale, sign bit = the
+// scale's): the code's sign bit is XOR-ed in, so the result's sign is the
+// product of both signs (zeros included).
+__device__ __forceinline__ void dequant_word_signed(uint32_t codes, uint32_t lut_hi, uint32_t lut_lo,
+                                                    uint32_t &even, uint32_t &odd)
+{
+    const uint32_t mag_e = byte_perm(lut_hi, lut_lo, codes & 0x07070707u);
+    const uint32_t mag_o = byte_perm(lut_hi, lut_lo, (codes >> 4) & 0x07070707u);
+    even = mag_e ^ ((codes << 4) & 0x80808080u);
+    odd = mag_o ^ (codes & 0x80808080u);
+}
+
+__device__ __forceinline__ void score_page(PageRegs &p, const uint32_t sc[8],
+                                           const uint64_t *lut, const RequestRegs &rq,
+                                           __amdgpu_buffer_rsrc_t nsrc, int m, int g, float &r0,
+                                           float &r1)
 {
     const float ninf = -__builtin_huge_valf();
     v4f mx0 = {ninf, ninf, ninf, ninf};
     v4f mx1 = mx0;
-    bool nan = false;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         // The fence keeps the compiler from hoisting the selector arithmetic
@@ -239,18 +258,11 @@ __device__ __forceinline__ void score_page(const PageRegs &p, const uint32_t sc[
         v4f c1 = c0;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            const uint32_t s = (sc[t] >> (8 * hh)) & 0xFFu;
-            const uint64_t e = lut[s];
-            uint32_t flip = 0;
-            if (kGeneral) {
-                flip = scale_sign_flip(s);
-                nan |= scale_is_nan(s);
-            }
+            const uint64_t e = lut[(sc[t] >> (8 * hh)) & 0xFFu];
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 uint32_t ev, od;
-                dequant_word(kGeneral ? w[2 * hh + k] ^ flip : w[2 * hh + k], uint32_t(e >> 32),
-                             uint32_t(e), ev, od);
+                dequant_word_signed(w[2 * hh + k], uint32_t(e >> 32), uint32_t(e), ev, od);
                 const v8h av = __builtin_bit_cast(v8h, f16_word(ev, od));
                 c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                     av, __builtin_bit_cast(v8h, rq.qa[2 * hh + k]), c0, 0, 0, 0);
@@ -258,6 +270,9 @@ __device__ __forceinline__ void score_page(const PageRegs &p, const uint32_t sc[
                     av, __builtin_bit_cast(v8h, rq.qb[2 * hh + k]), c1, 0, 0, 0);
             }
         }
+        // This tile's code registers are free: they take the next page's.
+        p.codes[t] = __builtin_amdgcn_raw_buffer_load_b128(nsrc, (16 * t + m) * 64 + 16 * g, 0,
+                                                           kStreamLoad);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             mx0[i] = fmaxf(mx0[i], c0[i]);
@@ -273,20 +288,17 @@ __device__ __forceinline__ void score_page(const PageRegs &p, const uint32_t sc[
     m1 = fmaxf(m1, __shfl_xor(m1, 32));
     r0 = m0;
     r1 = m1;
-    page_nan = kGeneral ? __any(nan) : false;
 }
 
-// True when some scale byte of the page is negative or NaN, i.e. not in
-// 0x00..0x7E: then the page takes the general path.  Per byte, bit 7 of
-// byte | (byte + 1) is set exactly when byte >= 0x7F; a carry out of a 0xFF
-// byte can only flag its neighbour as well, which merely costs the fast path.
-__device__ __forceinline__ bool page_needs_general(const PageRegs &p)
+// True when some scale byte of the page is NaN (0x7F or 0xFF): every dot
+// of that token is NaN, so the page's score is.
+__device__ __forceinline__ bool page_has_nan_scale(const PageRegs &p)
 {
-    uint32_t f = 0;
+    bool nan = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        f |= p.scales[i] | (p.scales[i] + 0x01010101u);
-    return __any((f & 0x80808080u) != 0);
+        nan |= has_nan_byte(p.scales[i]);
+    return __any(nan);
 }
 
 __global__ __launch_bounds__(256, 2) void score_decode_kernel(
@@ -347,11 +359,12 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
     // empty descriptor): after a conditional load the compiler could not
     // count the loads in flight and would wait for the page before the
     // query conversion below.
-    PageRegs pa, pb;
-    bool ok_a = false, ok_b = false;
-    fetch_page(pa, page_src(j0, ok_a), lane, m, g);
+    PageRegs pr;
+    bool cur_ok = false;
+    fetch_page(pr, page_src(j0, cur_ok), lane, m, g);
 
-    lut[tid] = lut_entry_g;
+    // Signed table: a negative scale's entry carries the sign bit.
+    lut[tid] = lut_entry_g | ((tid & 0x80) ? 0x8080808080808080ull : 0ull);
     RequestRegs rq;
     finish_request(rq, qraw, seq, qlen, lane);
     if (logical % gx == 0 && wave == 0 && row_own && lane < kDecodeRows)
@@ -360,40 +373,27 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
     if (j0 >= j1)
         return;
 
-    int j = j0;
-    // Issue the next page's loads into `nxt` (after the run's last page the
-    // descriptor is empty and the loads cost nothing), then score page j
-    // from `cur`.
-    auto step = [&](const PageRegs &cur, bool cur_ok, PageRegs &nxt, bool &nxt_ok) -> bool {
-        fetch_page(nxt, page_src(j + 1 < j1 ? j + 1 : j1, nxt_ok), lane, m, g);
-        // Keep the next page's loads ahead of everything that reads this
-        // page: scheduled after the scale unpacking they would wait for this
-        // page's last load, leaving nothing in flight.
-        __builtin_amdgcn_sched_barrier(0);
-        if (cur_ok) {
-            uint32_t sc[8];
-            unpack_scales(cur, stage, lane, m, g, sc);
-            float r0, r1;
-            bool page_nan;
-            if (page_needs_general(cur))
-                score_page<true>(cur, sc, lut, rq, r0, r1, page_nan);
-            else
-                score_page<false>(cur, sc, lut, rq, r0, r1, page_nan);
-            if (lane < kDecodeRows && j < rq.own) {
-                const float v = lane < 16 ? r0 : r1;
-                float s = (v + fabsf(v)) * 0.5f * rq.qs;
-                if (page_nan || rq.qnan)
-                    s = __builtin_nanf("");
-                scores[((int64_t)b * kDecodeRows + lane) * width + j] = s;
-            }
+    // One set of page registers, refilled as it is consumed: the next page's
+    // scale block is requested once this page's is staged, and its codes
+    // tile by tile as this page's tiles are scored.  Past the run's last
+    // page the descriptor is empty and the loads cost nothing.
+    for (int j = j0; j < j1; ++j) {
+        bool nxt_ok;
+        const __amdgpu_buffer_rsrc_t nsrc = page_src(j + 1 < j1 ? j + 1 : j1, nxt_ok);
+        uint32_t sc[8];
+        unpack_scales(pr, stage, lane, m, g, sc);
+        const bool page_nan = page_has_nan_scale(pr);
+        pr.scales = __builtin_amdgcn_raw_buffer_load_b128(nsrc, kCodeBytes + 16 * lane, 0, kStreamLoad);
+        float r0, r1;
+        score_page(pr, sc, lut, rq, nsrc, m, g, r0, r1);
+        if (cur_ok && lane < kDecodeRows && j < rq.own) {
+            const float v = lane < 16 ? r0 : r1;
+            float s = (v + fabsf(v)) * 0.5f * rq.qs;
+            if (page_nan || rq.qnan)
+                s = __builtin_nanf("");
+            scores[((int64_t)b * kDecodeRows + lane) * width + j] = s;
         }
-        return ++j < j1;
-    };
-    for (;;) {
-        if (!step(pa, ok_a, pb, ok_b))
-            break;
-        if (!step(pb, ok_b, pa, ok_a))
-            break;
+        cur_ok = nxt_ok;
     }
 }
 
