@@ -155,15 +155,22 @@ __device__ __forceinline__ int32_t pages_scored(int32_t seq, int32_t width)
     return n < width ? n : width;
 }
 
+// The score row a lane stores once a page's maxima are joined across lanes:
+// lanes 0..15 rows 0..15, lanes 32..47 rows 16..31, others none (-1).
+__device__ __forceinline__ int store_row(int lane)
+{
+    return lane < 16 ? lane : (lane >= 32 && lane < 48 ? lane - 16 : -1);
+}
+
 struct RequestRegs {
     u32x4 qa[4], qb[4];  // B operands (f16): query rows m and 16+m, chunk g, per code word
-    int own;             // lanes 0..31: own page of row `lane`
-    float qs;            // lanes 0..31: q_scale of row `lane`
-    bool qnan;           // lanes 0..31: row `lane` has a NaN query byte
+    int own;             // own page of row store_row(lane) (-1 for other lanes)
+    float qs;            // q_scale of that row
+    bool qnan;           // that row has a NaN query byte
 };
 
 // Raw query bytes (rows m and 16+m, depth chunk g) and the q_scale of row
-// `lane`, as loaded; slots without a query are not read.
+// store_row(lane), as loaded; slots without a query are not read.
 struct RequestRaw {
     uint32_t bytes[2][8];
     float qs;
@@ -189,8 +196,9 @@ __device__ __forceinline__ void load_request_raw(RequestRaw &r, const uint8_t *_
             r.bytes[hf][i] = w[i];
     }
     r.qs = 0.0f;
-    if (lane < kDecodeRows && lane / kDecodeHeads >= kSlots - qlen)
-        r.qs = q_scale[(int64_t)b * kDecodeRows + lane];
+    const int row = store_row(lane);
+    if (row >= 0 && row / kDecodeHeads >= kSlots - qlen)
+        r.qs = q_scale[(int64_t)b * kDecodeRows + row];
 }
 
 __device__ __forceinline__ void finish_request(RequestRegs &rq, const RequestRaw &r, int32_t seq,
@@ -212,10 +220,11 @@ __device__ __forceinline__ void finish_request(RequestRegs &rq, const RequestRaw
         f |= __shfl_xor(f, 32);
         nan_half[hf] = f != 0;
     }
-    if (lane < kDecodeRows) {
-        rq.own = decode_own(seq, qlen, lane / kDecodeHeads);
+    const int row = store_row(lane);
+    if (row >= 0) {
+        rq.own = decode_own(seq, qlen, row / kDecodeHeads);
         rq.qs = r.qs;
-        rq.qnan = lane < 16 ? nan_half[0] : nan_half[1];
+        rq.qnan = row < 16 ? nan_half[0] : nan_half[1];
     } else {
         rq.own = -1;
         rq.qs = 0.0f;
@@ -223,9 +232,6 @@ __device__ __forceinline__ void finish_request(RequestRegs &rq, const RequestRaw
     }
 }
 
-// Score one page for the request's 32 rows: the per-lane maxima r0 (row m)
-// and r1 (row 16+m) of the raw dot products, and whether a NaN scale byte
-// makes the whole page NaN.
 // Dequantize the 8 E2M1 codes of one word against a signed table entry
 // (byte c = E4M3 of code magnitude c times the scale, sign bit = the
 // scale's): the code's sign bit is XOR-ed in, so the result's sign is the
@@ -239,10 +245,13 @@ __device__ __forceinline__ void dequant_word_signed(uint32_t codes, uint32_t lut
     odd = mag_o ^ (codes & 0x80808080u);
 }
 
+// Score one page for the request's 32 rows: rmax is the page maximum of the
+// raw dot products of row store_row(lane).  Each tile's code registers are
+// refilled from nsrc (the next page) once the tile is scored.
 __device__ __forceinline__ void score_page(PageRegs &p, const uint32_t sc[8],
                                            const uint64_t *lut, const RequestRegs &rq,
-                                           __amdgpu_buffer_rsrc_t nsrc, int m, int g, float &r0,
-                                           float &r1)
+                                           __amdgpu_buffer_rsrc_t nsrc, int lane, int m, int g,
+                                           float &rmax)
 {
     const float ninf = -__builtin_huge_valf();
     v4f mx0 = {ninf, ninf, ninf, ninf};
@@ -280,14 +289,19 @@ __device__ __forceinline__ void score_page(PageRegs &p, const uint32_t sc[8],
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    float m0 = fmaxf(fmaxf(mx0[0], mx0[1]), fmaxf(mx0[2], mx0[3]));
-    float m1 = fmaxf(fmaxf(mx1[0], mx1[1]), fmaxf(mx1[2], mx1[3]));
-    m0 = fmaxf(m0, __shfl_xor(m0, 16));
-    m0 = fmaxf(m0, __shfl_xor(m0, 32));
-    m1 = fmaxf(m1, __shfl_xor(m1, 16));
-    m1 = fmaxf(m1, __shfl_xor(m1, 32));
-    r0 = m0;
-    r1 = m1;
+    const float m0 = fmaxf(fmaxf(mx0[0], mx0[1]), fmaxf(mx0[2], mx0[3]));
+    const float m1 = fmaxf(fmaxf(mx1[0], mx1[1]), fmaxf(mx1[2], mx1[3]));
+    // Join the four depth-chunk lanes of each row with two lane swaps: the
+    // 32-lane swap pairs m0's halves in lanes 0..31 and m1's in 32..63, the
+    // 16-lane swap finishes both.  Lane m then holds row m and lane 32 + m
+    // row 16 + m (see store_row).
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(m0), __float_as_uint(m1), false,
+                                                    false);
+    float x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    x = fmaxf(x, __uint_as_float((lane & 16) ? q[0] : q[1]));
+    rmax = x;
 }
 
 // True when some scale byte of the page is NaN (0x7F or 0xFF): every dot
@@ -335,7 +349,7 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
     // table and the query rows.  The first page is requested as soon as the
     // length and the ids are in; the table, the query conversion and the
     // barrier come after, while that page is in flight.
-    const int32_t seq = seq_lens[b];
+    const int32_t seq = __builtin_amdgcn_readfirstlane(seq_lens[b]);
     int32_t id_lane = -1;
     if (lane < chunk && j0 + lane < width)
         id_lane = block_table[(int64_t)b * bt_stride + j0 + lane];
@@ -367,8 +381,8 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
     lut[tid] = lut_entry_g | ((tid & 0x80) ? 0x8080808080808080ull : 0ull);
     RequestRegs rq;
     finish_request(rq, qraw, seq, qlen, lane);
-    if (logical % gx == 0 && wave == 0 && row_own && lane < kDecodeRows)
-        row_own[(int64_t)b * kDecodeRows + lane] = rq.own;
+    if (logical % gx == 0 && wave == 0 && row_own && store_row(lane) >= 0)
+        row_own[(int64_t)b * kDecodeRows + store_row(lane)] = rq.own;
     __syncthreads();
     if (j0 >= j1)
         return;
@@ -384,14 +398,14 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
         unpack_scales(pr, stage, lane, m, g, sc);
         const bool page_nan = page_has_nan_scale(pr);
         pr.scales = __builtin_amdgcn_raw_buffer_load_b128(nsrc, kCodeBytes + 16 * lane, 0, kStreamLoad);
-        float r0, r1;
-        score_page(pr, sc, lut, rq, nsrc, m, g, r0, r1);
-        if (cur_ok && lane < kDecodeRows && j < rq.own) {
-            const float v = lane < 16 ? r0 : r1;
+        float v;
+        score_page(pr, sc, lut, rq, nsrc, lane, m, g, v);
+        // Lanes without a row have own = -1 and store nothing.
+        if (cur_ok && j < rq.own) {
             float s = (v + fabsf(v)) * 0.5f * rq.qs;
             if (page_nan || rq.qnan)
                 s = __builtin_nanf("");
-            scores[((int64_t)b * kDecodeRows + lane) * width + j] = s;
+            scores[((int64_t)b * kDecodeRows + store_row(lane)) * width + j] = s;
         }
         cur_ok = nxt_ok;
     }
