@@ -359,6 +359,11 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
 
     const int np = pages_scored(seq, width);
     const int j1 = j0 + chunk < np ? j0 + chunk : np;
+    // A work-group past the request's last page leaves as soon as the length
+    // is in (the first work-group of a request stays: it writes row_own).
+    // Ragged batches launch many such groups.
+    if (logical % gx != 0 && (logical % gx) * kWavesPerBlock * chunk >= np)
+        return;
 
     // Descriptor of page j: empty past the run and for an id out of range
     // (such a page is not scored).  The id is read with v_readlane, so the
@@ -420,11 +425,13 @@ hipError_t launch_score_decode(const uint8_t *kv, int64_t page_stride, int64_t n
                                int32_t *row_own, int num_cus, hipStream_t stream)
 {
     // Pages per wave: the batch's upper bound of pages spread over about eight
-    // waves per compute unit (two resident work-groups of four), 1..16.
+    // waves per compute unit (two resident work-groups of four), 1..8.  Past
+    // 8, ragged batches (whose upper bound is far above their real pages)
+    // lose more to the last runs than they save on per-run set-up.
     const int64_t max_pages = (int64_t)num_reqs * width;
     const int64_t waves = (int64_t)(num_cus > 0 ? num_cus : 256) * 8;
     int64_t chunk = (max_pages + waves - 1) / waves;
-    chunk = chunk < 1 ? 1 : (chunk > 16 ? 16 : chunk);
+    chunk = chunk < 1 ? 1 : (chunk > 8 ? 8 : chunk);
     const int64_t gx = ((int64_t)width + chunk * kWavesPerBlock - 1) / (chunk * kWavesPerBlock);
     hipLaunchKernelGGL(score_decode_kernel, dim3((uint32_t)gx, (uint32_t)num_reqs), dim3(256), 0,
                        stream, kv, page_stride, num_blocks, block_table, bt_stride, seq_lens, q,
