@@ -37,7 +37,9 @@
 //
 // In a pass, a new key whose high word is below that of the wave's current
 // 16th key cannot enter its best 16 and is dropped before selection; a pass
-// that keeps no new key costs one compare and ballot per slot.
+// that keeps no new key costs one compare and ballot per slot, and one that
+// keeps at most 48 sorts them with the 16 held keys directly, without the
+// threshold step.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -251,16 +253,26 @@ template <int N>
 __device__ __forceinline__ uint64_t wave_top16(const Candidates<N> &c, uint64_t *surv, int lane)
 {
     const uint32_t held_hi = (uint32_t)(c.held >> 32);
-    uint32_t lmax = held_hi;
+    // With 16 keys held, the caller's floor has dropped every key below the
+    // 16th: usually only a few are left, and when the held keys and those
+    // fit in 64 lanes they are placed and sorted directly, without the
+    // threshold step.
+    int total = kWave + 1;
+    if (readlane_u64(c.held, kTopk - 1) != 0)
+        total = place_survivors(
+            c, [&](int i) { return i < 0 ? c.held != 0 : c.hi[i] != 0; }, surv, lane);
+    if (total > kWave) {
+        uint32_t lmax = held_hi;
 #pragma unroll
-    for (int i = 0; i < N; ++i)
-        lmax = c.hi[i] > lmax ? c.hi[i] : lmax;
-    uint32_t t = __builtin_amdgcn_readlane(wave_sort_desc<64>(lmax, lane), kTopk - 1);
-    t = t > 0 ? t : 1;   // real keys only
+        for (int i = 0; i < N; ++i)
+            lmax = c.hi[i] > lmax ? c.hi[i] : lmax;
+        uint32_t t = __builtin_amdgcn_readlane(wave_sort_desc<64>(lmax, lane), kTopk - 1);
+        t = t > 0 ? t : 1;   // real keys only
 
-    // Survivors: keys whose high word reaches t.
-    int total = place_survivors(
-        c, [&](int i) { return (i < 0 ? held_hi : c.hi[i]) >= t; }, surv, lane);
+        // Survivors: keys whose high word reaches t.
+        total = place_survivors(
+            c, [&](int i) { return (i < 0 ? held_hi : c.hi[i]) >= t; }, surv, lane);
+    }
     if (total > kWave) {
         // Ties on the high word: the exact 16th key (at least 16 keys exist,
         // since more than 64 survived), and exactly 16 survivors.
