@@ -160,7 +160,8 @@ int indexer_score_prefill(const uint8_t *q, const float *q_scale, const uint8_t 
  * append_page is given and append_page[r] >= 0, then -1 up to 16 entries;
  * k = 15 when append_page is given, else 16.
  *
- *   scores         [num_rows, row_stride] float32, row_stride >= width >= 1.
+ *   scores         [num_rows, row_stride] float32, row_stride >= width >= 1;
+ *                  width above 268,435,456 is PAGESCORE_EINVAL.
  *   valid_len      nullable [num_rows] int32 (NULL: every row has width).
  *   force_begin/force_end  nullable [num_rows] int32 (both or neither).
  *   append_page    nullable [num_rows] int32 (decode: the rows' own pages).

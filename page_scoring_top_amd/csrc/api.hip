@@ -103,7 +103,7 @@ int topk16_select(const float *scores, int64_t row_stride, int32_t num_rows, int
                   const int32_t *valid_len, const int32_t *force_begin, const int32_t *force_end,
                   const int32_t *append_page, int32_t *out, int64_t out_stride, void *stream)
 {
-    if (num_rows < 0 || width < 1)
+    if (num_rows < 0 || width < 1 || width > pagescore::kTopkMaxWidth)
         return PAGESCORE_EINVAL;
     if (num_rows == 0)
         return PAGESCORE_OK;

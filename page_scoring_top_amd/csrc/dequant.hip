@@ -29,12 +29,7 @@ constexpr int kStreamLoad = 2;    // buffer cache policy: nontemporal (read once
 // page of its run, whether the page exists or not.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t *page, bool live)
 {
-    const uint64_t a = reinterpret_cast<uintptr_t>(page);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    const int records = __builtin_amdgcn_readfirstlane(live ? kPageBytes : 0);
-    return __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), (short)0, records, 0x00020000);
+    return uniform_rsrc(page, live ? kPageBytes : 0u);
 }
 
 // One page in registers: round i (tokens 16 i .. 16 i + 15) is 1 KiB of

@@ -66,4 +66,20 @@ __device__ __forceinline__ bool scale_is_nan(uint32_t scale_byte)
     return (scale_byte & 0x7Fu) == 0x7Fu;
 }
 
+// A raw buffer descriptor over `bytes` bytes at `base` (wave-uniform by
+// construction).  Loads at or past `bytes` read zeros and stores there are
+// dropped, without touching memory; a descriptor of 0 bytes makes every
+// access free.  The fields go through v_readfirstlane so the descriptor sits
+// in scalar registers (one the compiler cannot prove uniform costs a loop
+// per access); the address halves are widened as unsigned values.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uintptr_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), (short)0, (int)n, 0x00020000);
+}
+
 }  // namespace pagescore

@@ -15,6 +15,10 @@ constexpr int32_t kDequantMaxReqs = 65535;
 // rows (heads rounded up to 32) as f16 in LDS.
 constexpr int32_t kPrefillMaxHeads = 224;
 
+// Columns per topk16_select row: a wave reads its share of a row through a
+// buffer descriptor whose byte size and offsets are 32-bit.
+constexpr int32_t kTopkMaxWidth = 1 << 28;
+
 hipError_t launch_nvfp4_dequant(const uint8_t *kv, int64_t page_stride, int64_t num_blocks,
                                 const int32_t *block_table, int64_t bt_stride,
                                 const int32_t *num_pages, const int32_t *page_offsets,

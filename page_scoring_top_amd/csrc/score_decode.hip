@@ -81,17 +81,9 @@ struct PageRegs {
 // the same loads for every page, whether it exists or not.
 constexpr int kStreamLoad = 2;   // cache policy: nontemporal (streamed once)
 
-// The fields go through v_readfirstlane: they are wave-uniform by
-// construction, and this keeps the descriptor in scalar registers (a
-// descriptor the compiler cannot prove uniform costs a loop per load).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t *page, bool live)
 {
-    const uint64_t a = reinterpret_cast<uintptr_t>(page);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    const int records = __builtin_amdgcn_readfirstlane(live ? kPageBytes : 0);
-    return __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), (short)0, records, 0x00020000);
+    return uniform_rsrc(page, live ? kPageBytes : 0u);
 }
 
 // The scale block first, as the page loop refills it: the first page's loads

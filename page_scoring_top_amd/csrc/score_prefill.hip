@@ -157,15 +157,6 @@ constexpr int kSmallHeads = 64;
 constexpr int kMaxKeysPerGroup = 1 << 20;                     // keeps descriptor sizes in 32 bits
 constexpr uint32_t kDropped = 0x80000000u;                    // an offset past every descriptor
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t bounded_rsrc(const void *base, uint32_t bytes)
-{
-    const uint64_t a = reinterpret_cast<uintptr_t>(base);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), (short)0, (int)n, 0x00020000);
-}
 
 __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel(
     const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
@@ -224,9 +215,9 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
         // Keys [kb + 128 c, ke): a chunk past the range has no records.
         const int base = kb + c * kChunkKeys;
         const int live = c < chunks ? (ke - base < kChunkKeys ? ke - base : kChunkKeys) : 0;
-        const __amdgpu_buffer_rsrc_t kr = bounded_rsrc(k + (int64_t)(c < chunks ? base : 0) * kDepth,
+        const __amdgpu_buffer_rsrc_t kr = uniform_rsrc(k + (int64_t)(c < chunks ? base : 0) * kDepth,
                                                        (uint32_t)live * kDepth);
-        const __amdgpu_buffer_rsrc_t sr = bounded_rsrc(k_scale + (c < chunks ? base : 0),
+        const __amdgpu_buffer_rsrc_t sr = uniform_rsrc(k_scale + (c < chunks ? base : 0),
                                                        (uint32_t)live * 4);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -245,7 +236,7 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
 
     // Scores of this token for keys [kb, ke); other tokens have no records.
     const __amdgpu_buffer_rsrc_t out =
-        bounded_rsrc(scores + (tok_ok ? t : 0) * ld + kb, tok_ok ? (uint32_t)(ke - kb) * 4u : 0u);
+        uniform_rsrc(scores + (tok_ok ? t : 0) * ld + kb, tok_ok ? (uint32_t)(ke - kb) * 4u : 0u);
 
     // The drain of a tile's accumulators is cut into 16 slices, one per MFMA
     // of the next tile.  Element e (0..31) is row e % 16 of head tile e / 16;

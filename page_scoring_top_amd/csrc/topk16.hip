@@ -52,17 +52,16 @@ constexpr int kWideLane = 16;                      // columns per lane and pass 
 constexpr int kNarrowLane = 4;                     // for rows of at most 256 columns
 constexpr int kBlockWaves = 4;                     // one wave per SIMD
 
-// Order-preserving image of the canonical score (never 0).
-__device__ __forceinline__ uint32_t key_hi(float s, int col, int fb, int fe)
+// Order-preserving image of the canonical score (never 0).  Adding +0
+// turns -0 into +0 and quiets a NaN, and the IEEE maximum with -inf then
+// returns -inf for a NaN and the value itself otherwise; a forced column is
+// +inf.  The map sets the sign bit of a positive value and flips every bit
+// of a negative one.
+__device__ __forceinline__ uint32_t key_hi(float s, bool forced)
 {
-    uint32_t u = __float_as_uint(s);
-    if (col >= fb && col < fe)
-        u = 0x7F800000u;                       // forced: +inf
-    else if ((u & 0x7FFFFFFFu) > 0x7F800000u)
-        u = 0xFF800000u;                       // NaN: -inf
-    else if (u == 0x80000000u)
-        u = 0u;                                // -0: +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const float c = __builtin_fmaxf(s + 0.0f, -__builtin_huge_valf());
+    const uint32_t u = forced ? 0x7F800000u : __float_as_uint(c);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ uint64_t make_key(uint32_t hi, int col)
@@ -328,18 +327,21 @@ __global__ __launch_bounds__(256) void topk16_kernel(
     // This wave's columns: whole 64-column groups of the width, split evenly;
     // the row's valid length trims them once it is known.  The first pass is
     // requested together with the row's parameters (every lane loads every
-    // slot, a column past the end reading the last one, so the loads issue
-    // back to back with no branch between them).
+    // slot, so the loads issue back to back with no branch between them).
     const int groups = (width + kWave - 1) / kWave;
     const int span = ((groups + waves_per_row - 1) / waves_per_row) * kWave;
     const int c0 = part * span;
     const int cw = live ? (c0 + span < width ? c0 + span : width) : c0;   // loadable end
+    // Columns [c0, cw) of the row through a descriptor: a column past cw
+    // reads as zero, and the loads of a pass differ only in their immediate
+    // offsets.
+    const __amdgpu_buffer_rsrc_t rsrc = uniform_rsrc(srow + c0, (uint32_t)(cw - c0) * 4u);
     auto load = [&](int pc, float (&v)[kPerLane]) {
+        const uint32_t off = (uint32_t)(pc - c0 + lane) * 4u;
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
-            const int col = pc + i * kWave + lane;
-            v[i] = srow[col < cw ? col : cw - 1];
-        }
+        for (int i = 0; i < kPerLane; ++i)
+            v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 rsrc, off + i * kWave * 4, 0, 0));
     };
     float v[kPerLane];
     if (c0 < cw)
@@ -354,6 +356,7 @@ __global__ __launch_bounds__(256) void topk16_kernel(
         ap = append_page ? append_page[row] : -1;
     }
     const int c1 = cw < n ? cw : n;   // this wave's candidates: [c0, c1)
+    const uint32_t fspan = fe > fb ? (uint32_t)(fe - fb) : 0u;   // forced columns [fb, fe)
 
     uint64_t best = 0;   // lane r < 16: this partition's r-th best key so far
     for (int pc = c0; pc < c1; pc += kPassCols) {
@@ -364,17 +367,26 @@ __global__ __launch_bounds__(256) void topk16_kernel(
         cand.base = pc;
         cand.held = best;
         // Keys whose high word is below the current 16th best cannot enter.
+        // Column checks are unsigned ranges: col - fb < fe - fb (forced) and,
+        // in the pass that reaches c1, lane < c1 - (pc + 64 i).
         const uint32_t floor_hi = (uint32_t)(readlane_u64(best, kTopk - 1) >> 32);
-        bool any_new = false;
+        const int rel = pc - fb + lane;
+        uint32_t hmax = 0;
 #pragma unroll
         for (int i = 0; i < kPerLane; ++i) {
-            const int col = pc + i * kWave + lane;
-            uint32_t h = col < c1 ? key_hi(v[i], col, fb, fe) : 0u;
+            uint32_t h = key_hi(v[i], (uint32_t)(rel + i * kWave) < fspan);
             h = h >= floor_hi ? h : 0u;
-            any_new |= h != 0;
             cand.hi[i] = h;
         }
-        if (__any(any_new))
+        if (pc + kPassCols > c1) {
+#pragma unroll
+            for (int i = 0; i < kPerLane; ++i)
+                cand.hi[i] = lane < c1 - pc - i * kWave ? cand.hi[i] : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i)
+            hmax = cand.hi[i] > hmax ? cand.hi[i] : hmax;
+        if (__any(hmax != 0))
             best = wave_top16(cand, surv[wave], lane);
         if (pc + kPassCols < c1) {
 #pragma unroll

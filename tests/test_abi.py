@@ -138,6 +138,7 @@ def test_topk_host_checks(lib):
     assert _topk(lib, rows=0) == 0
     assert _topk(lib, rows=-1) == EINVAL
     assert _topk(lib, W=0) == EINVAL
+    assert _topk(lib, W=(1 << 28) + 1, rs=(1 << 28) + 1) == EINVAL   # width past the limit
     assert _topk(lib, rs=99) == EINVAL
     assert _topk(lib, os=15) == EINVAL
     assert _topk(lib, fb=FAKE) == EINVAL                 # begin without end

@@ -42,6 +42,34 @@ def test_injected_rows(width):
                                                np.argwhere((got != want).any(1))[:4].ravel())
 
 
+@pytest.mark.parametrize("width", [300, 5000])
+def test_special_bit_patterns(width):
+    """Subnormals of both signs next to +-0, NaNs with payloads (quiet and
+    signalling, both signs), +-inf and FLT_MAX: the key of each must order as
+    its canonical score (NaN as -inf, -0 as +0)."""
+    rng = np.random.default_rng(width + 11)
+    bits = np.array([0x00000001, 0x80000001, 0x007FFFFF, 0x807FFFFF, 0x00400000, 0x80000000,
+                     0x00000000, 0x7FC00000, 0xFFC00000, 0x7F800001, 0xFF800001, 0x7FFFFFFF,
+                     0xFFFFFFFF, 0x7F800000, 0xFF800000, 0x7F7FFFFF, 0xFF7FFFFF, 0x00800000],
+                    dtype=np.uint32)
+    rows = 16
+    s = rng.standard_normal((rows, width)).astype(np.float32)
+    u = s.view(np.uint32)
+    for r in range(rows):
+        k = int(rng.integers(width // 4, width))           # special patterns over most columns
+        cols = rng.choice(width, size=k, replace=False)
+        u[r, cols] = bits[rng.integers(0, len(bits), size=k)]
+    s[1] = np.where(rng.random(width) < 0.5, np.float32(1e-45), np.float32(-1e-45))
+    s[2] = np.float32(-1e-45)                                  # all equal subnormals
+    fb = rng.integers(0, width, size=rows).astype(np.int32)
+    fe = (fb + rng.integers(0, 4, size=rows)).astype(np.int32)
+    announce(f"topk special bit patterns width={width}")
+    for kw in (dict(), dict(fb=fb, fe=fe)):
+        got = gpu_topk(s, width, **kw)
+        want = oracle.topk16(s, None, kw.get("fb"), kw.get("fe"), None)
+        assert np.array_equal(got, want), np.argwhere((got != want).any(1))[:4].ravel()
+
+
 def test_prefill_width_rows():
     """2,048-row x 16,384-column buffer, the prefill score shape, in the benchmark's
     launch configuration (sampled rows compared; all rows are exact by construction)."""
