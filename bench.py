@@ -21,6 +21,7 @@ bounded sample of the same workload.
   python bench.py --profile-pass     # short fixed sequence for rocprofv3 counter runs
   python bench.py --workload prefill # lightning-indexer prefill step (scores + top-16)
   python bench.py --workload dequant # NVFP4 gather-dequantize of the decode pages
+  python bench.py --workload nvfp4-prefill  # NVFP4 pages gathered, scored (4 heads), top-16
 """
 
 from __future__ import annotations
@@ -77,7 +78,8 @@ def parse():
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
-    ap.add_argument("--workload", choices=("decode", "prefill", "dequant"), default="decode")
+    ap.add_argument("--workload", choices=("decode", "prefill", "dequant", "nvfp4-prefill"),
+                    default="decode")
     return ap.parse_args()
 
 
@@ -170,6 +172,98 @@ def bench_prefill(args):
     print(json.dumps(result), flush=True)
 
 
+def bench_nvfp4_prefill(args):
+    """Q8KV8 prefill chain: 512 NVFP4 pages (a 65,536-token context) gathered
+    into E4M3 keys, 2,048 query tokens x 4 heads scored against them with unit
+    key scales, then the top-16 of every score row."""
+    import torch
+
+    import page_scoring_top_amd as ps
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    d = workloads.nvfp4_prefill()
+    T, H = d.q.shape[0], d.q.shape[1]
+    N = int(d.context[0])
+    P = d.total_pages
+    kv = torch.from_numpy(d.kv_cache).to(dev)
+    bt = torch.from_numpy(d.block_table).to(dev)
+    num_pages = torch.from_numpy(d.num_pages).to(dev)
+    offs = torch.from_numpy(d.page_offsets).to(dev)
+    q = torch.from_numpy(d.q).to(dev)
+    qs = torch.from_numpy(d.q_scale).to(dev)
+    keys = torch.empty((P, 128, 128), dtype=torch.uint8, device=dev)
+    ones = torch.ones(N, dtype=torch.float32, device=dev)
+    scores = torch.empty((T, N), dtype=torch.float32, device=dev)
+    out = torch.empty((T, 16), dtype=torch.int32, device=dev)
+    gather_call = ps.prepare(ps.nvfp4_index_k_dequant, kv, bt, num_pages, offs,
+                             d.block_table.shape[1], keys)
+    score_call = ps.prepare(ps.indexer_score_prefill, q, qs, keys.view(-1, 128)[:N], ones, scores)
+    topk_call = ps.prepare(ps.topk16_select, scores, N, out)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        gather_call()
+        score_call()
+        topk_call()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    ms_per_step = timed(torch, stream, step, K)
+    gather_ms = timed(torch, stream, lambda i: gather_call(), K)
+    score_ms = timed(torch, stream, lambda i: score_call(), K)
+    topk_ms = timed(torch, stream, lambda i: topk_call(), K)
+    # Score kernel: queries, scales and keys read once, every score written once.
+    algo = T * H * (128 + 4) + N * (128 + 4) + T * N * 4
+    achieved = algo / (score_ms * 1e-3) / 1e9
+    pairs = T * N
+    result = {
+        "metric": "NVFP4 (Q8KV8) prefill: query-key scores per second, gather + scores + top-16",
+        "value": round(pairs / (ms_per_step * 1e-3) / 1e9, 3),
+        "unit": "G scores/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "e4m3 values as f16, f32 accumulate", "data": "synthetic",
+        "config": {"workload": "NVFP4 prefill: 512 pages (65,536-token context) gathered to E4M3, "
+                               "2,048 tokens x 4 heads x depth 128 scored, top-16 of 2,048 rows",
+                   "tokens": T, "heads": H, "keys": N, "pages": P, "parallelism": "single GPU"},
+        "kernels_us": {"nvfp4_index_k_dequant": round(gather_ms * 1e3, 3),
+                       "indexer_score_prefill": round(score_ms * 1e3, 3),
+                       "topk16_select": round(topk_ms * 1e3, 3)},
+        "roofline": {"bound": "hbm", "kernel": "indexer_score_prefill",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": algo},
+    }
+    if not args.no_cpu:
+        import numpy as np
+        import oracle
+        t0 = time.perf_counter()
+        keys_ora = oracle.gather(d.kv_cache, d.block_table, d.num_pages, d.page_offsets,
+                                 d.block_table.shape[1],
+                                 np.empty((P, 128, 128), dtype=np.uint8)).reshape(-1, 128)[:N]
+        t_gather = time.perf_counter() - t0
+        ones_h = np.ones(N, dtype=np.float32)
+        t1 = time.perf_counter()
+        n = 0
+        while n < T and time.perf_counter() - t1 < args.cpu_seconds:
+            row = oracle.score_prefill_rows(d.q, d.q_scale, keys_ora, ones_h, [n])
+            oracle.topk16(row)
+            n += 1
+        t_rows = time.perf_counter() - t1
+        cpu_step = t_gather + t_rows * T / n
+        result["cpu_baseline"] = {
+            "value": round(pairs / cpu_step / 1e9, 9), "unit": "G scores/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"oracle gather of all {P} pages ({t_gather:.2f} s), then scores and top-16 "
+                      f"of {n} full rows ({t_rows:.2f} s) scaled to {T} rows; "
+                      f"step estimate {cpu_step:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def bench_dequant(args):
     """Gather-dequantize of every scored page of the 500K-token decode batch
     (15,624 pages) into contiguous E4M3 pages, rotating over index-K pools."""
@@ -253,6 +347,8 @@ def main():
         return bench_prefill(args)
     if args.workload == "dequant":
         return bench_dequant(args)
+    if args.workload == "nvfp4-prefill":
+        return bench_nvfp4_prefill(args)
 
     import numpy as np
 

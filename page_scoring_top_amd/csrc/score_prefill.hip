@@ -131,9 +131,10 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
 // keys streamed through LDS, the epilogue of one key tile run between the
 // MFMAs of the next.
 //
-// A wave holds its token's 64 query rows as f16 A operands (two 32-head
-// tiles x eight 16-deep K steps = 64 VGPRs) and the q_scale of the 32 heads
-// its accumulator lanes hold (32 VGPRs).  The work-group's eight waves (two
+// A wave holds its token's query rows as f16 A operands (kHT = 1 or 2
+// 32-head tiles x eight 16-deep K steps = 32 kHT VGPRs) and the q_scale of
+// the heads its accumulator lanes hold (16 kHT VGPRs); up to 32 heads take
+// one tile and half the MFMAs of 64.  The work-group's eight waves (two
 // per SIMD) convert the keys to f16 together, 128 keys at a time, into three
 // rotating LDS buffers; one barrier per 128 keys.  Rows of the key buffer
 // are padded to 272 bytes so the 32 keys a B read touches fall on distinct
@@ -156,8 +157,17 @@ constexpr int kKeyRowBytes = kRowHalves * 2;                  // 272
 constexpr int kSmallHeads = 64;
 constexpr int kMaxKeysPerGroup = 1 << 20;                     // keeps descriptor sizes in 32 bits
 constexpr uint32_t kDropped = 0x80000000u;                    // an offset past every descriptor
+constexpr uint32_t kKeyDropped = 0x40000000u;                 // added to a row offset: past it too
+constexpr int kPackHeads = 4;                                 // heads per token, packed
+constexpr int64_t kPackMaxLd = 1 << 24;                       // 16 rows of scores <= 2^30 bytes
 
 
+// kPack: up to four heads, a wave takes 8 kHT tokens and row 4 u + h of its
+// A tile ht is head h of token 8 ht + u.  In the accumulator, element i of
+// tile ht is then head i % 4 of token 8 ht + 2 (i / 4) + half, so the head
+// sum of a (token, key) score is four elements of one lane, and a lane
+// stores 4 kHT scores per tile.
+template <int kHT, bool kPack>
 __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel(
     const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
     const uint8_t *__restrict__ k, const float *__restrict__ k_scale, int32_t T, int32_t H,
@@ -170,20 +180,23 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
     const int lane = tid % kWave;
     const int col = lane & 31;
     const int half = lane >> 5;
-    const int64_t t = (int64_t)blockIdx.x * kH64Waves + wave;
+    constexpr int kTokPerWave = kPack ? 8 * kHT : 1;
+    const int64_t t = ((int64_t)blockIdx.x * kH64Waves + wave) * kTokPerWave;
     const bool tok_ok = t < T;
+    const int tok_rows = !tok_ok ? 0 : (T - t < kTokPerWave ? (int)(T - t) : kTokPerWave);
     const int kb = blockIdx.y * keys_per_group;
     const int ke = kb + keys_per_group < N ? kb + keys_per_group : N;
     const int chunks = (ke - kb + kChunkKeys - 1) / kChunkKeys;
 
     // Query rows as f16 A operands: head 32 ht + col, depth 16 st + 8 half
-    // .. +8 (zero past H, and for a token past T).
-    u32x4 a[2][8];
+    // .. +8 (zero past H, and for a token past T); kHT head tiles of 32.
+    u32x4 a[kHT][8];
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-        const int h = 32 * ht + col;
-        const bool ok = tok_ok && h < H;
-        const uint8_t *src = q + ((ok ? t : 0) * H + (ok ? h : 0)) * kDepth + 8 * half;
+    for (int ht = 0; ht < kHT; ++ht) {
+        const int h = kPack ? col % 4 : 32 * ht + col;
+        const int u = kPack ? 8 * ht + col / 4 : 0;
+        const bool ok = u < tok_rows && h < H;
+        const uint8_t *src = q + ((ok ? t + u : 0) * H + (ok ? h : 0)) * kDepth + 8 * half;
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
             uint2 b = make_uint2(0u, 0u);
@@ -193,14 +206,16 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
         }
     }
     // Scales of the heads the lane's accumulators hold: element i of tile ht
-    // is head 32 ht + 8 (i / 4) + 4 half + i % 4.
-    float qs[2][16];
+    // is head 32 ht + 8 (i / 4) + 4 half + i % 4 (packed: head i % 4 of
+    // token 8 ht + 2 (i / 4) + half).
+    float qs[kHT][16];
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
+    for (int ht = 0; ht < kHT; ++ht)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int h = 32 * ht + 8 * (i / 4) + 4 * half + i % 4;
-            qs[ht][i] = (tok_ok && h < H) ? q_scale[t * H + h] : 0.0f;
+            const int h = kPack ? i % 4 : 32 * ht + 8 * (i / 4) + 4 * half + i % 4;
+            const int u = kPack ? 8 * ht + 2 * (i / 4) + half : 0;
+            qs[ht][i] = (u < tok_rows && h < H) ? q_scale[(t + u) * H + h] : 0.0f;
         }
 
     // Key conversion: thread -> key tid / 4 of the chunk, 32 depth bytes at
@@ -234,25 +249,49 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
             ks_lds[buf][ck] = r.ks;
     };
 
-    // Scores of this token for keys [kb, ke); other tokens have no records.
-    const __amdgpu_buffer_rsrc_t out =
-        uniform_rsrc(scores + (tok_ok ? t : 0) * ld + kb, tok_ok ? (uint32_t)(ke - kb) * 4u : 0u);
+    // Scores of this wave's tokens for keys [kb, ke); a wave past T has no
+    // records.  Packed, the descriptor spans the wave's rows (at most 2^30
+    // bytes), and a store's offset is row_off[g], the byte offset of the
+    // lane's row of token 8 (g / 4) + 2 (g % 4) + half (kDropped for a token
+    // past T), plus the key's offset (plus kKeyDropped for a key past ke):
+    // every dropped offset lies past the records, and none wraps.
+    const __amdgpu_buffer_rsrc_t out = uniform_rsrc(
+        scores + (tok_ok ? t : 0) * ld + kb,
+        tok_ok ? (uint32_t)(((int64_t)(tok_rows - 1) * ld + (ke - kb)) * 4) : 0u);
+    const int key_count = ke - kb;
+    uint32_t row_off[kPack ? 4 * kHT : 1];
+    if constexpr (kPack) {
+#pragma unroll
+        for (int g = 0; g < 4 * kHT; ++g) {
+            const int u = 8 * (g / 4) + 2 * (g % 4) + half;
+            row_off[g] = u < tok_rows ? (uint32_t)(u * ld * 4) : kDropped;
+        }
+    }
 
-    // The drain of a tile's accumulators is cut into 16 slices, one per MFMA
-    // of the next tile.  Element e (0..31) is row e % 16 of head tile e / 16;
+    // The drain of a tile's accumulators is cut into 8 kHT slices, one per
+    // MFMA of the next tile.  Element e (0 .. 16 kHT - 1) is row e % 16 of
+    // head tile e / 16;
     // its doubled relu y = x + |x| is formed one slice before its fma, so no
     // VALU instruction waits on the one just before it, and the fma goes to
-    // partial sum e % 4.
-    v16f acc[2][2];
+    // partial sum e % 4 (packed: the sum of its token, e / 4).  A sum's first
+    // term is a multiply.
+    constexpr int kElems = 16 * kHT;
+    constexpr int kParts = kPack ? 4 * kHT : 4;
+    v16f acc[2][kHT];
     float y[4];
-    float part[4];
-    auto drain_slice = [&](const v16f (&c)[2], int m) {
+    float part[kParts];
+    auto part_of = [](int e) { return kPack ? e / 4 : e % 4; };
+    auto first_of_part = [](int e) { return kPack ? e % 4 == 0 : e < 4; };
+    auto add_term = [&](int e) {
+        const float v = y[e % 4];
+        const float w = qs[e / 16][e % 16];
+        part[part_of(e)] = first_of_part(e) ? v * w : fmaf(v, w, part[part_of(e)]);
+    };
+    auto drain_slice = [&](const v16f (&c)[kHT], int m) {
         if (m > 0) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int e = 2 * (m - 1) + j;
-                part[e % 4] = fmaf(y[(e % 4)], qs[e / 16][e % 16], part[e % 4]);
-            }
+            for (int j = 0; j < 2; ++j)
+                add_term(2 * (m - 1) + j);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -266,8 +305,18 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
     // relative to kb, and a negative one drops the store).
     auto drain_tail = [&](float ks, int n_rel) {
 #pragma unroll
-        for (int e = 30; e < 32; ++e)
-            part[e % 4] = fmaf(y[e % 4], qs[1][e % 16], part[e % 4]);
+        for (int e = kElems - 2; e < kElems; ++e)
+            add_term(e);
+        if constexpr (kPack) {
+            const int n = n_rel + col;
+            const uint32_t key_off = (n_rel >= 0 && n < key_count) ? (uint32_t)n * 4u : kKeyDropped;
+            const float hks = 0.5f * ks;
+#pragma unroll
+            for (int g = 0; g < kParts; ++g)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hks * part[g]), out,
+                                                      row_off[g] + key_off, 0, 0);
+            return;
+        }
         const float sum = (part[0] + part[1]) + (part[2] + part[3]);
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum),
                                                          false, false);
@@ -301,8 +350,9 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
 
     // acc[p]: the tile being accumulated and the tile being drained swap
     // roles every tile.  The drain before the first tile stores nothing.
-    acc[1][0] = v16f{};
-    acc[1][1] = v16f{};
+#pragma unroll
+    for (int ht = 0; ht < kHT; ++ht)
+        acc[1][ht] = v16f{};
     float ks_prev = 0.0f;
     int n_prev = -1;
     u32x4 b_carry[2] = {read_b(0, 0, 0), read_b(0, 0, 1)};
@@ -319,15 +369,14 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
         b[0][1] = b_carry[1];
 #pragma unroll
         for (int kt = 0; kt < kTilesPerChunk; ++kt) {
-            v16f (&cur)[2] = acc[kt & 1];
-            const v16f (&prev)[2] = acc[(kt & 1) ^ 1];
-            part[0] = part[1] = part[2] = part[3] = 0.0f;
+            v16f (&cur)[kHT] = acc[kt & 1];
+            const v16f (&prev)[kHT] = acc[(kt & 1) ^ 1];
             const float ks = ks_lds[buf][kt * kKeysPerTile + col];
 #pragma unroll
             for (int st = 0; st < 8; ++st) {
 #pragma unroll
-                for (int ht = 0; ht < 2; ++ht) {
-                    const int m = 2 * st + ht;
+                for (int ht = 0; ht < kHT; ++ht) {
+                    const int m = kHT * st + ht;
                     cur[ht] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                         __builtin_bit_cast(v8h, a[ht][st]), __builtin_bit_cast(v8h, b[kt][st]),
                         st == 0 ? v16f{} : cur[ht], 0, 0, 0);
@@ -340,9 +389,9 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
                         else
                             b_carry[st - 6] = read_b(nbuf, 0, st - 6);
                     }
-                    // The last tile converts chunk c + 2, one piece every
-                    // other MFMA.
-                    if (kt == kTilesPerChunk - 1 && ht == 1 && st < 4)
+                    // The last tile converts chunk c + 2, one piece per
+                    // K step.
+                    if (kt == kTilesPerChunk - 1 && ht == kHT - 1 && st < 4)
                         store_piece(nxt, wbuf, st);
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -356,9 +405,8 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
         buf = nbuf;
     }
     // Drain the last tile.
-    part[0] = part[1] = part[2] = part[3] = 0.0f;
 #pragma unroll
-    for (int m = 0; m < 16; ++m)
+    for (int m = 0; m < 8 * kHT; ++m)
         drain_slice(acc[(kTilesPerChunk - 1) & 1], m);
     drain_tail(ks_prev, n_prev);
 }
@@ -373,11 +421,16 @@ hipError_t launch_score_prefill(const uint8_t *q, const float *q_scale, const ui
                                 float *scores, int64_t ld, hipStream_t stream)
 {
     if (H <= kSmallHeads) {
-        // One token per wave, eight per work-group (one work-group per
-        // compute unit fits).  The keys are split so the grid holds about one
-        // work-group per compute unit, in whole chunks of 128 keys and at
-        // most 2^20 keys per work-group.
-        const int64_t groups = ((int64_t)T + kH64Waves - 1) / kH64Waves;
+        // One token per wave (eight packed tokens up to four heads), eight
+        // waves per work-group (one work-group per compute unit fits).  The
+        // keys are split so the grid holds about one work-group per compute
+        // unit, in whole chunks of 128 keys and at most 2^20 keys per
+        // work-group.
+        // Up to four heads, 16 tokens per wave (8 for a short prefill).
+        const bool pack = H <= kPackHeads && ld <= kPackMaxLd;
+        const int pack_tiles = T > 8 * kH64Waves ? 2 : 1;
+        const int64_t tokens_per_group = (int64_t)kH64Waves * (pack ? 8 * pack_tiles : 1);
+        const int64_t groups = ((int64_t)T + tokens_per_group - 1) / tokens_per_group;
         if (groups > 0x7FFFFFFF)
             return hipErrorInvalidValue;
         const int64_t chunks = ((int64_t)N + kChunkKeys - 1) / kChunkKeys;
@@ -389,9 +442,21 @@ hipError_t launch_score_prefill(const uint8_t *q, const float *q_scale, const ui
         splits = ((int64_t)N + keys_per_group - 1) / keys_per_group;
         if (splits > 65535)
             return hipErrorInvalidValue;
-        hipLaunchKernelGGL(score_prefill_h64_kernel, dim3((uint32_t)groups, (uint32_t)splits),
-                           dim3(kH64Waves * kWave), 0, stream, q, q_scale, k, k_scale, T, H, N,
-                           (int32_t)keys_per_group, scores, ld);
+        const dim3 grid((uint32_t)groups, (uint32_t)splits), block(kH64Waves * kWave);
+        // Packed tokens up to four heads; otherwise one 32-head MFMA tile up
+        // to 32 heads, two up to 64.
+        if (pack && pack_tiles == 2)
+            hipLaunchKernelGGL((score_prefill_h64_kernel<2, true>), grid, block, 0, stream, q, q_scale,
+                               k, k_scale, T, H, N, (int32_t)keys_per_group, scores, ld);
+        else if (pack)
+            hipLaunchKernelGGL((score_prefill_h64_kernel<1, true>), grid, block, 0, stream, q, q_scale,
+                               k, k_scale, T, H, N, (int32_t)keys_per_group, scores, ld);
+        else if (H <= 32)
+            hipLaunchKernelGGL((score_prefill_h64_kernel<1, false>), grid, block, 0, stream, q, q_scale,
+                               k, k_scale, T, H, N, (int32_t)keys_per_group, scores, ld);
+        else
+            hipLaunchKernelGGL((score_prefill_h64_kernel<2, false>), grid, block, 0, stream, q, q_scale,
+                               k, k_scale, T, H, N, (int32_t)keys_per_group, scores, ld);
         return hipGetLastError();
     }
     const int hp = (H + 31) & ~31;

@@ -24,7 +24,26 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
-def assert_scores_close(got: np.ndarray, want: np.ndarray, what: str = "") -> None:
+def prefill_term_magnitude(q, q_scale, k, k_scale) -> np.ndarray:
+    """k_scale[n] * sum_h |q_scale[t,h]| * sum_d |q[t,h,d] k[n,d]| in float64:
+    the size of the terms a prefill score is summed from.  An f32 sum of
+    them carries an error of a few units in the last place of this size, not
+    of the result, so a score whose dot products cancel is compared against
+    it.  (E4M3 bytes are read through torch's float8_e4m3fn, exactly.)"""
+    def val(b):
+        return torch.from_numpy(np.ascontiguousarray(b)).view(torch.float8_e4m3fn).double().abs()
+    qa = val(q)                                   # [T, H, 128]
+    ka = val(k)                                   # [N, 128]
+    qs = torch.from_numpy(np.asarray(q_scale, dtype=np.float64)).abs()
+    ks = torch.from_numpy(np.asarray(k_scale, dtype=np.float64)).abs()
+    dots = torch.matmul(qa, ka.T.contiguous())    # [T, H, N]
+    return ((dots * qs[:, :, None]).sum(dim=1) * ks[None, :]).numpy()
+
+
+def assert_scores_close(got: np.ndarray, want: np.ndarray, what: str = "",
+                        magnitude: np.ndarray | None = None) -> None:
+    """|got - want| <= ATOL + RTOL * |want|; with ``magnitude`` (the size of
+    the summed terms, for sums that cancel) RTOL scales max(|want|, magnitude)."""
     got = np.asarray(got, dtype=np.float32)
     want = np.asarray(want, dtype=np.float32)
     assert got.shape == want.shape, (got.shape, want.shape)
@@ -34,7 +53,10 @@ def assert_scores_close(got: np.ndarray, want: np.ndarray, what: str = "") -> No
     assert np.array_equal(gi, wi) and np.array_equal(got[gi], want[wi]), f"{what}: inf differ"
     fin = ~(wn | wi)
     err = np.abs(got[fin].astype(np.float64) - want[fin].astype(np.float64))
-    lim = ATOL + RTOL * np.abs(want[fin].astype(np.float64))
+    scale = np.abs(want[fin].astype(np.float64))
+    if magnitude is not None:
+        scale = np.maximum(scale, np.asarray(magnitude, dtype=np.float64)[fin])
+    lim = ATOL + RTOL * scale
     bad = err > lim
     if bad.any():
         idx = np.argwhere(fin)[np.argmax(err / lim)]

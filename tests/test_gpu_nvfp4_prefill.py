@@ -1,0 +1,130 @@
+"""GPU parity of the NVFP4 prefill chain (Q8KV8 prefill indexer, vLLM API page
+``gather_nvfp4_index_k``, module description): each request's NVFP4 index-K
+pages are gathered into contiguous E4M3 keys by nvfp4_index_k_dequant, its
+queries are scored against the first ``context`` keys by
+indexer_score_prefill with every key scale 1 (the pages carry no global
+scale), and topk16_select picks the 16 best keys of every query row.
+
+Each stage is checked against the oracle on the same inputs: the gathered
+bytes exactly, the scores against the oracle's scores of the oracle's
+gathered keys, and the top-16 exactly against the oracle's selection over the
+GPU's own score rows.
+
+Score tolerance.  Block scales span the whole positive E4M3 range, so keys
+reach 448 and a token's dot products can cancel to a result far below their
+terms; an f32 accumulation is then off by a few units in the last place of
+the terms, not of the result.  Scores are compared with
+|gpu - oracle| <= 1e-6 + 1e-5 max(|oracle|, M), M = k_scale * sum_h q_scale *
+sum_d |q k| (the size of the summed terms), and at most 0.1% of them may need
+M, i.e. fall outside 1e-6 + 1e-5 |oracle|."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import (ATOL, CANARY_F32, CANARY_I32, RTOL, announce, assert_scores_close, dev, host,
+                      prefill_term_magnitude)
+
+pytestmark = pytest.mark.gpu
+
+
+def gather_gpu(d: workloads.Nvfp4PrefillInputs, extra_pages: int = 1):
+    import page_scoring_top_amd as ps
+    total = d.total_pages
+    out = torch.full((total + extra_pages, 128, 128), 0xA5, dtype=torch.uint8, device="cuda")
+    ps.nvfp4_index_k_dequant(dev(d.kv_cache), dev(d.block_table), dev(d.num_pages),
+                             dev(d.page_offsets), d.block_table.shape[1], out)
+    return out
+
+
+def gather_oracle(d: workloads.Nvfp4PrefillInputs, extra_pages: int = 1):
+    out = np.full((d.total_pages + extra_pages, 128, 128), 0xA5, dtype=np.uint8)
+    return oracle.gather(d.kv_cache, d.block_table, d.num_pages, d.page_offsets,
+                         d.block_table.shape[1], out)
+
+
+def request_keys(keys, d, b):
+    """Keys [context[b], 128] of request b inside the gathered pages."""
+    off = int(d.page_offsets[b])
+    return keys[off:off + int(d.num_pages[b])].reshape(-1, 128)[:int(d.context[b])]
+
+
+def check_scores(got, want, magnitude, what):
+    assert_scores_close(got, want, what, magnitude=magnitude)
+    fin = np.isfinite(want)
+    plain = np.abs(got[fin].astype(np.float64) - want[fin]) <= ATOL + RTOL * np.abs(want[fin])
+    assert (~plain).sum() <= 1e-3 * fin.sum(), f"{what}: {(~plain).sum()} scores need the term bound"
+
+
+def run_chain(d: workloads.Nvfp4PrefillInputs, keys_gpu):
+    """Per request: scores [tokens, context + 2] (two canary columns) and
+    top-16 ids, on the GPU."""
+    import page_scoring_top_amd as ps
+    res = []
+    t0 = 0
+    for b in range(len(d.tokens)):
+        T, N = int(d.tokens[b]), int(d.context[b])
+        q = dev(d.q[t0:t0 + T])
+        qs = dev(d.q_scale[t0:t0 + T])
+        k = request_keys(keys_gpu, d, b)
+        ones = torch.ones(N, dtype=torch.float32, device="cuda")
+        scores = torch.full((T, N + 2), float(CANARY_F32), dtype=torch.float32, device="cuda")
+        ps.indexer_score_prefill(q, qs, k, ones, scores)
+        ids = torch.full((T, 16), int(CANARY_I32), dtype=torch.int32, device="cuda")
+        ps.topk16_select(scores, N, ids)
+        res.append((scores, ids))
+        t0 += T
+    return res
+
+
+@pytest.mark.parametrize("tokens,contexts,heads", [
+    ([37, 100, 1], [1000, 3000, 129], 4),   # ragged token groups and key tails
+    ([64], [128], 4),                       # whole tiles only
+    ([20, 9], [300, 17], 1),
+    ([11], [700], 3),
+    ([5], [260], 8),                        # more heads than one packed tile holds
+])
+def test_chain_small(tokens, contexts, heads):
+    d = workloads.nvfp4_prefill_inputs("nvfp4-prefill-small", 100 + sum(contexts) + heads,
+                                       tokens, contexts, heads)
+    announce(f"nvfp4 prefill chain tokens={tokens} contexts={contexts} heads={heads}")
+    keys_gpu = gather_gpu(d)
+    keys_ora = gather_oracle(d)
+    assert np.array_equal(host(keys_gpu), keys_ora), "gathered E4M3 keys differ"
+    t0 = 0
+    for b, (scores, ids) in enumerate(run_chain(d, keys_gpu)):
+        T, N = int(d.tokens[b]), int(d.context[b])
+        got = host(scores)
+        ones = np.ones(N, dtype=np.float32)
+        k_ora = request_keys(keys_ora, d, b)
+        want = oracle.score_prefill(d.q[t0:t0 + T], d.q_scale[t0:t0 + T], k_ora, ones)
+        mag = prefill_term_magnitude(d.q[t0:t0 + T], d.q_scale[t0:t0 + T], k_ora, ones)
+        check_scores(got[:, :N], want, mag, f"request {b}")
+        assert (got[:, N:].view(np.int32) == CANARY_F32.view(np.int32)).all(), "store past context"
+        assert np.array_equal(host(ids), oracle.topk16(got[:, :N])), f"request {b}: top-16 differ"
+        t0 += T
+
+
+def test_chain_long_context_sampled():
+    """A 2,048-token chunk with 4 heads against a 65,536-token context (512
+    pages), in the benchmark's launch configuration: every gathered byte,
+    full score rows of tokens at the edges of waves and work-groups, and the
+    top-16 of those rows."""
+    d = workloads.nvfp4_prefill()
+    announce("nvfp4 prefill 2048 x 4 heads x 65536 keys")
+    keys_gpu = gather_gpu(d, extra_pages=0)
+    keys_ora = gather_oracle(d, extra_pages=0)
+    assert np.array_equal(host(keys_gpu), keys_ora), "gathered E4M3 keys differ"
+    (scores, ids), = run_chain(d, keys_gpu)
+    rows = [0, 1, 7, 8, 63, 64, 1029, 2040, 2047]
+    got = host(scores[rows])
+    N = int(d.context[0])
+    k_ora = request_keys(keys_ora, d, 0)
+    ones = np.ones(N, dtype=np.float32)
+    want = oracle.score_prefill_rows(d.q, d.q_scale, k_ora, ones, rows)
+    mag = prefill_term_magnitude(d.q[rows], d.q_scale[rows], k_ora, ones)
+    check_scores(got[:, :N], want, mag, "long-context prefill")
+    assert (got[:, N:].view(np.int32) == CANARY_F32.view(np.int32)).all()
+    assert np.array_equal(host(ids)[rows], oracle.topk16(got[:, :N]))

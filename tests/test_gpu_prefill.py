@@ -25,7 +25,10 @@ def gpu_prefill(p: workloads.PrefillInputs, ld=None):
                                    (17, 64, 257), (4, 65, 130),
                                    # many 128-key chunks, a ragged last chunk and token
                                    # group, key ranges split over several work-groups
-                                   (13, 48, 1000), (2, 64, 5000), (8, 64, 128), (9, 1, 129)])
+                                   (13, 48, 1000), (2, 64, 5000), (8, 64, 128), (9, 1, 129),
+                                   # up to four heads, eight tokens per wave: ragged last
+                                   # wave and work-group, several token groups
+                                   (67, 4, 1000), (130, 2, 300), (513, 4, 2000), (64, 4, 128)])
 def test_small_shapes_full(T, H, N):
     p = workloads.prefill_inputs("small", T * 1000 + H * 10 + N, T, H, N)
     announce(f"prefill T={T} H={H} N={N}")

@@ -170,6 +170,58 @@ def big_prefill(seed: int = 4) -> PrefillInputs:
     return prefill_inputs("prefill", seed, 2048, 64, 16384)
 
 
+@dataclasses.dataclass
+class Nvfp4PrefillInputs:
+    """Prefill queries scored against NVFP4 index-K pages gathered into
+    contiguous E4M3 keys (the Q8KV8 prefill of the vLLM API page
+    ``gather_nvfp4_index_k``): request ``b`` has ``tokens[b]`` queries (rows
+    ``sum(tokens[:b])`` onward of ``q``) and ``context[b]`` keys on its first
+    ``ceil(context[b] / 128)`` block-table pages."""
+    name: str
+    kv_cache: np.ndarray      # [num_blocks, 9216] uint8
+    block_table: np.ndarray   # [R, bt_cols] int32
+    context: np.ndarray       # [R] int32
+    num_pages: np.ndarray     # [R] int32
+    page_offsets: np.ndarray  # [R] int32: first gathered page of each request
+    tokens: np.ndarray        # [R] int32
+    q: np.ndarray             # [sum(tokens), H, 128] uint8 (E4M3 bytes)
+    q_scale: np.ndarray       # [sum(tokens), H] float32
+
+    @property
+    def total_pages(self) -> int:
+        return int(self.num_pages.sum())
+
+
+def nvfp4_prefill_inputs(name: str, seed: int, tokens, contexts, heads: int = DECODE_HEADS,
+                         spare_pages: int = 3) -> Nvfp4PrefillInputs:
+    """Each request's pages are a random permutation of a shared physical pool
+    (with ``spare_pages`` pages that no request uses)."""
+    st = _streams(seed)
+    tokens = np.asarray(tokens, dtype=np.int32)
+    context = np.asarray(contexts, dtype=np.int32)
+    npages = ((context.astype(np.int64) + PAGE_TOKENS - 1) // PAGE_TOKENS).astype(np.int32)
+    nb = int(npages.sum()) + spare_pages
+    kv = random_pages(st[_S_CODES], st[_S_SCALES], nb)
+    perm = st[_S_TABLE].permutation(nb).astype(np.int32)
+    bt = np.zeros((len(context), max(int(npages.max()), 1)), dtype=np.int32)
+    offs = np.zeros(len(context), dtype=np.int32)
+    off = 0
+    for b, n in enumerate(npages):
+        bt[b, :n] = perm[off:off + n]
+        offs[b] = off
+        off += int(n)
+    Tt = int(tokens.sum())
+    q = e4m3_bytes_from_normal(st[_S_Q], (Tt, heads, HEAD_DIM))
+    qs = st[_S_QSCALE].uniform(0.5, 2.0, size=(Tt, heads)).astype(np.float32)
+    return Nvfp4PrefillInputs(name, kv, bt, context, npages, offs, tokens, q, qs)
+
+
+def nvfp4_prefill(seed: int = 6) -> Nvfp4PrefillInputs:
+    """One request: a 2,048-token prefill chunk with 4 index heads against a
+    65,536-token context (512 NVFP4 pages)."""
+    return nvfp4_prefill_inputs("nvfp4-prefill", seed, [2048], [65536])
+
+
 # ---------------------------------------------------------------------------
 # Score rows with injected special values, for the top-16 selection.
 # ---------------------------------------------------------------------------
