@@ -159,6 +159,11 @@ constexpr int kMaxKeysPerGroup = 1 << 20;                     // keeps descripto
 constexpr uint32_t kDropped = 0x80000000u;                    // an offset past every descriptor
 constexpr uint32_t kKeyDropped = 0x40000000u;                 // added to a row offset: past it too
 constexpr int kPackHeads = 4;                                 // heads per token, packed
+// Cache policy of the packed path's score stores: nontemporal (the "nt"
+// bit).  Its 16 score rows per wave are written at four bytes per key and
+// never read back by the kernel; measured 11% faster than default stores
+// at 2,048 tokens x 65,536 keys.
+constexpr int kStreamingStore = 2;
 constexpr int64_t kPackMaxLd = 1 << 24;                       // 16 rows of scores <= 2^30 bytes
 
 
@@ -314,7 +319,7 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
 #pragma unroll
             for (int g = 0; g < kParts; ++g)
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hks * part[g]), out,
-                                                      row_off[g] + key_off, 0, 0);
+                                                      row_off[g] + key_off, 0, kStreamingStore);
             return;
         }
         const float sum = (part[0] + part[1]) + (part[2] + part[3]);
