@@ -142,6 +142,12 @@ int indexer_score_decode(const uint8_t *kv_cache, int64_t page_stride_bytes,
  *   scores   [T, ld] float32 with ld >= N; columns >= N are not written.
  * T == 0 or N == 0 returns PAGESCORE_OK with no launch; 1 <= H <= 224 (a
  * work-group holds one token's query rows as f16 in 64 KiB of LDS).
+ *
+ * NVFP4 prefill ([GATHER] module description, the Q8KV8 prefill indexer):
+ * nvfp4_index_k_dequant gathers a request's pages into contiguous E4M3 pages,
+ * whose first `context` rows are k here with k_scale all ones (the page
+ * format has no global scale); topk16_select then keeps each query row's 16
+ * best keys.
  */
 int indexer_score_prefill(const uint8_t *q, const float *q_scale, const uint8_t *k,
                           const float *k_scale, int32_t T, int32_t H, int32_t N,
