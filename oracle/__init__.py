@@ -62,6 +62,9 @@ def lib():
             "ora_score_prefill_rows": (None, [P, P, P, P, I32, I32, P, I32, P]),
             "ora_rank_value": (D, [ctypes.c_float, ctypes.c_int]),
             "ora_topk16": (None, [P, I64, I32, I32, P, P, P, P, P, I64]),
+            "ora_bf16_value": (D, [ctypes.c_int]),
+            "ora_mx_block_scale": (ctypes.c_int, [P]),
+            "ora_mxfp8_quantize": (None, [P, I64, I32, I32, P, I64, P, I64]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -217,3 +220,30 @@ def topk16(scores, valid_len=None, force_begin=None, force_end=None, append_page
     vl, fb, fe, ap = (_c(a, np.int32) for a in (valid_len, force_begin, force_end, append_page))
     lib().ora_topk16(_p(s), width, rows, width, _p(vl), _p(fb), _p(fe), _p(ap), _p(out), 16)
     return out
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 quantization
+# ---------------------------------------------------------------------------
+
+def bf16_value(bits: int) -> float:
+    return lib().ora_bf16_value(int(bits))
+
+
+def mx_block_scale(block) -> int:
+    """E8M0 byte of one block of 32 bf16 bit patterns."""
+    b = _c(block, np.uint16).reshape(-1)
+    assert b.size == 32
+    return lib().ora_mx_block_scale(_p(b))
+
+
+def mxfp8_quantize(x):
+    """``x [rows, cols]`` bf16 bit patterns (uint16, cols a multiple of 32) ->
+    (E4M3 bytes ``[rows, cols]``, E8M0 bytes ``[rows, cols / 32]``)."""
+    x = _c(x, np.uint16)
+    rows, cols = x.shape
+    assert cols % 32 == 0
+    q = np.empty((rows, cols), dtype=np.uint8)
+    s = np.empty((rows, cols // 32), dtype=np.uint8)
+    lib().ora_mxfp8_quantize(_p(x), cols, rows, cols, _p(q), cols, _p(s), cols // 32)
+    return q, s

@@ -20,6 +20,8 @@
  *            (lightning-indexer score and its branchless relu).
  *   [MSA]    GitHub pull request wolfcomos/MSA #1: "Changes" and "Behaviour
  *            changes" sections (candidate order).
+ *   [ROCM]   vLLM pull request #65508 (ROCm MXFP8 epilogue): "How it works",
+ *            arithmetic item (E8M0 block scale and E4M3 rounding).
  *
  * Readings taken where the pages leave a step open are marked READING.
  * Parity pins for every function are in the test suite.
@@ -403,4 +405,74 @@ void ora_topk16(const float *scores, int64_t row_stride, int32_t num_rows, int32
             o[pos] = -1;
     }
     free(c);
+}
+
+/* ------------------------------------------------------------------------
+ * [ROCM] MXFP8 E4M3 quantization of bf16 activations ("How it works",
+ * arithmetic item): blocks of 32 consecutive elements of a row share one
+ * E8M0 scale byte sb, taken from the block's largest magnitude (compared on
+ * the bf16 bit patterns with the sign cleared):
+ *     sb = clamp(exponent_field(amax) - 8 + (fraction(amax) > 0.75), 0, 254)
+ * which is ceil(log2(amax / 448)) + 127 because 448 = 1.75 * 2^8.  Each
+ * element is multiplied by 2^(127 - sb) (exact) and rounded to E4M3, nearest
+ * with ties to even.
+ * READING: an element that is +-inf or NaN quantizes to the canonical NaN
+ * byte 0x7F; its bit pattern still takes part in the block maximum.
+ * ---------------------------------------------------------------------- */
+
+/* The value of a bf16 bit pattern: sign, 8 exponent bits (bias 127), 7
+ * fraction bits; exponent 0 is subnormal (f * 2^-133). */
+double ora_bf16_value(int bits)
+{
+    int s = (bits >> 15) & 1, e = (bits >> 7) & 0xFF, f = bits & 0x7F;
+    double mag;
+    if (e == 0xFF)
+        mag = f ? NAN : INFINITY;
+    else if (e == 0)
+        mag = f * ldexp(1.0, -133);
+    else
+        mag = (1.0 + f / 128.0) * ldexp(1.0, e - 127);
+    return s ? -mag : mag;
+}
+
+/* E8M0 byte of one 32-element block. */
+int ora_mx_block_scale(const uint16_t *x)
+{
+    int amax = 0;
+    for (int i = 0; i < 32; ++i) {
+        int a = x[i] & 0x7FFF;
+        if (a > amax)
+            amax = a;
+    }
+    int exponent_field = amax >> 7;
+    int fraction_bits = amax & 0x7F;
+    int sb = exponent_field - 8 + (fraction_bits / 128.0 > 0.75 ? 1 : 0);
+    if (sb < 0)
+        sb = 0;
+    if (sb > 254)
+        sb = 254;
+    return sb;
+}
+
+/* Quantize rows x [rows, ld_x] bf16 (cols a multiple of 32) into
+ * q [rows, ld_q] E4M3 bytes and scales [rows, ld_s] E8M0 bytes. */
+void ora_mxfp8_quantize(const uint16_t *x, int64_t ld_x, int32_t rows, int32_t cols,
+                        uint8_t *q, int64_t ld_q, uint8_t *scales, int64_t ld_s)
+{
+    for (int32_t r = 0; r < rows; ++r) {
+        for (int32_t b = 0; b < cols / 32; ++b) {
+            const uint16_t *blk = x + r * ld_x + 32 * b;
+            int sb = ora_mx_block_scale(blk);
+            scales[r * ld_s + b] = (uint8_t)sb;
+            for (int i = 0; i < 32; ++i) {
+                double v = ora_bf16_value(blk[i]);
+                uint8_t out;
+                if (isnan(v) || isinf(v))
+                    out = 0x7F;
+                else
+                    out = (uint8_t)ora_e4m3_rn_satfinite(v * ldexp(1.0, 127 - sb));
+                q[r * ld_q + 32 * b + i] = out;
+            }
+        }
+    }
 }
