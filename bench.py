@@ -22,6 +22,7 @@ bounded sample of the same workload.
   python bench.py --workload prefill # lightning-indexer prefill step (scores + top-16)
   python bench.py --workload dequant # NVFP4 gather-dequantize of the decode pages
   python bench.py --workload nvfp4-prefill  # NVFP4 pages gathered, scored (4 heads), top-16
+  python bench.py --workload mxfp8   # MXFP8 quantization of the attention output
 """
 
 from __future__ import annotations
@@ -78,7 +79,8 @@ def parse():
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
-    ap.add_argument("--workload", choices=("decode", "prefill", "dequant", "nvfp4-prefill"),
+    ap.add_argument("--workload", choices=("decode", "prefill", "dequant", "nvfp4-prefill",
+                                           "mxfp8"),
                     default="decode")
     return ap.parse_args()
 
@@ -264,6 +266,101 @@ def bench_nvfp4_prefill(args):
     print(json.dumps(result), flush=True)
 
 
+def bench_mxfp8(args):
+    """MXFP8 quantization of the attention output (the step after the sparse
+    attention).  Timed: 16,384 rows x 2,048 bf16, a prefill-sized batch at
+    one tensor-parallel rank's 2,048 columns, rotating over six independent
+    input/output sets (610 MB, more than the 256 MB last-level cache) so each
+    launch streams from HBM.  Also reported: the 128 x 2,048 decode batch
+    (16 requests x 8 rows), which is launch-bound, timed as the pages time
+    it: 200 launches captured in one HIP graph, median of 15 replays."""
+    import torch
+
+    import page_scoring_top_amd as ps
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    rows, cols, P = 16384, 2048, 6
+    xh = workloads.mx_activations(5, rows, cols)
+    calls = []
+    for i in range(P):
+        x = torch.from_numpy(xh.view("int16")).to(dev).view(torch.bfloat16)
+        if i:
+            x = x.roll(i, dims=0).contiguous()
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        sc = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+        calls.append(ps.prepare(ps.mxfp8_e4m3_quantize, x, q, sc))
+    for i in range(args.warmup):
+        calls[i % P]()
+    torch.cuda.synchronize()
+    ms = timed(torch, stream, lambda i: calls[i % P](), args.steps)
+
+    # Decode batch in a graph.
+    dr = 128
+    xd = torch.from_numpy(workloads.mx_activations(6, dr, cols).view("int16")).to(dev).view(
+        torch.bfloat16)
+    qd = torch.empty((dr, cols), dtype=torch.uint8, device=dev)
+    sd = torch.empty((dr, cols // 32), dtype=torch.uint8, device=dev)
+    ps.mxfp8_e4m3_quantize(xd, qd, sd)
+    torch.cuda.synchronize()
+    q_eager, s_eager = qd.clone(), sd.clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(200):
+                ps.mxfp8_e4m3_quantize(xd, qd, sd)
+    torch.cuda.synchronize()
+    reps = []
+    for _ in range(15):
+        qd.zero_()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        if not (torch.equal(qd, q_eager) and torch.equal(sd, s_eager)):
+            raise RuntimeError("graph replay of mxfp8_e4m3_quantize differs from the eager result")
+        reps.append(a.elapsed_time(b) / 200 * 1e3)
+    decode_us = sorted(reps)[len(reps) // 2]
+
+    algo = rows * cols * 3 + rows * cols // 32
+    achieved = algo / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "MXFP8 quantization of bf16 activations, GB/s (bytes in + out)",
+        "value": round(achieved, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in, e4m3 + e8m0 out",
+        "data": "synthetic",
+        "config": {"workload": "MXFP8 (E4M3 + E8M0 per 32) quantization of 16,384 x 2,048 bf16 "
+                               "attention outputs, six rotating buffer sets",
+                   "rows": rows, "cols": cols, "buffer_sets": P, "parallelism": "single GPU"},
+        "kernels_us": {"mxfp8_e4m3_quantize": round(ms * 1e3, 3),
+                       "mxfp8_e4m3_quantize_128x2048_graph": round(decode_us, 3)},
+        "roofline": {"bound": "hbm", "kernel": "mxfp8_e4m3_quantize",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": algo},
+    }
+    if not args.no_cpu:
+        import oracle
+        t0 = time.perf_counter()
+        n = 0
+        while n < rows and time.perf_counter() - t0 < args.cpu_seconds:
+            oracle.mxfp8_quantize(xh[n:n + 64])
+            n += 64
+        t = time.perf_counter() - t0
+        cpu_step = t * rows / n
+        result["cpu_baseline"] = {
+            "value": round(algo / cpu_step / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle quantization of {n} rows ({t:.2f} s), scaled to {rows} rows"}
+    print(json.dumps(result), flush=True)
+
+
 def bench_dequant(args):
     """Gather-dequantize of every scored page of the 500K-token decode batch
     (15,624 pages) into contiguous E4M3 pages, rotating over index-K pools."""
@@ -349,6 +446,8 @@ def main():
         return bench_dequant(args)
     if args.workload == "nvfp4-prefill":
         return bench_nvfp4_prefill(args)
+    if args.workload == "mxfp8":
+        return bench_mxfp8(args)
 
     import numpy as np
 

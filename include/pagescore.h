@@ -1,7 +1,8 @@
 /*
  * pagescore.h -- C ABI of libpagescore.so, the gfx950 (MI355X) sparse-attention
  * indexer path: NVFP4 index-K dequantization, decode and prefill scores, and
- * the exact top-16 selection.
+ * the exact top-16 selection; and the MXFP8 quantization of the attention
+ * output that follows it.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -27,6 +28,7 @@
  *   [DECODE] vLLM API page "vllm.models.minimax_m3.nvidia.indexer_nvfp4_decode_cp"
  *   [MOJO]   Modular Mojo page "sparse_index_fp8_sm100"
  *   [MSA]    GitHub pull request wolfcomos/MSA #1 ("warp top-16")
+ *   [ROCM]   vLLM pull request #65508 (ROCm MXFP8 epilogue)
  */
 #ifndef PAGESCORE_H
 #define PAGESCORE_H
@@ -180,6 +182,29 @@ int topk16_select(const float *scores, int64_t row_stride, int32_t num_rows,
                   const int32_t *force_begin, const int32_t *force_end,
                   const int32_t *append_page, int32_t *out, int64_t out_stride,
                   void *stream);
+
+/*
+ * mxfp8_e4m3_quantize -- MXFP8 quantization of bf16 rows, the step after the
+ * sparse attention ([ROCM] "How it works": output layout and arithmetic).
+ * Each block of 32 consecutive elements of a row gets one E8M0 scale byte
+ *     sb = clamp(exponent_field(amax) - 8 + (fraction(amax) > 0.75), 0, 254)
+ * where amax is the block's largest magnitude compared on the bf16 bit
+ * patterns (sb = ceil(log2(amax / 448)) + 127), and each element becomes
+ * the E4M3 byte of x * 2^(127 - sb) rounded to nearest even.  Elements that
+ * are +-inf or NaN become 0x7F (canonical NaN).
+ *
+ *   x       [rows, x_stride] bf16 bit patterns, 16-byte aligned, x_stride a
+ *           multiple of 8 elements and >= cols.
+ *   cols    a multiple of 32.
+ *   q       [rows, q_stride] E4M3 bytes, 16-byte aligned, q_stride a multiple
+ *           of 16 and >= cols; only the first cols bytes of a row are written.
+ *   scales  [rows, scale_stride] E8M0 bytes, scale_stride >= cols / 32;
+ *           only the first cols / 32 bytes of a row are written.
+ * rows == 0 or cols == 0 returns PAGESCORE_OK with no launch.
+ */
+int mxfp8_e4m3_quantize(const uint16_t *x, int64_t x_stride, int32_t rows, int32_t cols,
+                        uint8_t *q, int64_t q_stride, uint8_t *scales, int64_t scale_stride,
+                        void *stream);
 
 /* HIP error code of the most recent PAGESCORE_ELAUNCH on this thread. */
 int pagescore_last_hip_error(void);

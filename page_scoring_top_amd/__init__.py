@@ -1,11 +1,13 @@
 """MI355X (gfx950) sparse-attention indexer path.
 
-Four calls, each a thin binding of the C ABI in include/pagescore.h:
+Five calls, each a thin binding of the C ABI in include/pagescore.h:
 
   nvfp4_index_k_dequant  -- gather NVFP4 index-K pages into contiguous E4M3 pages
   indexer_score_decode   -- fused NVFP4 dequant + per-page decode scores
   indexer_score_prefill  -- lightning-indexer scores summed over heads
   topk16_select          -- exact top-16 column ids per score row
+  mxfp8_e4m3_quantize    -- MXFP8 (E4M3 + E8M0) quantization of bf16 rows, the
+                            step after the sparse attention
 
 The kernels are hand-written HIP in csrc/, built by page_scoring_top_amd.build.
 """
@@ -16,10 +18,11 @@ from ._binding import (  # noqa: F401
     PreparedCall,
     indexer_score_decode,
     indexer_score_prefill,
+    mxfp8_e4m3_quantize,
     nvfp4_index_k_dequant,
     prepare,
     topk16_select,
 )
 
 __all__ = ["nvfp4_index_k_dequant", "indexer_score_decode", "indexer_score_prefill",
-           "topk16_select", "prepare", "PreparedCall", "PageScoreError", "LIB_PATH"]
+           "topk16_select", "mxfp8_e4m3_quantize", "prepare", "PreparedCall", "PageScoreError", "LIB_PATH"]

@@ -29,8 +29,9 @@ _lib.indexer_score_decode.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P, _P, _I32
                                       _P, _P, _P]
 _lib.indexer_score_prefill.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _P, _I64, _P]
 _lib.topk16_select.argtypes = [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _I64, _P]
+_lib.mxfp8_e4m3_quantize.argtypes = [_P, _I64, _I32, _I32, _P, _I64, _P, _I64, _P]
 for _f in (_lib.nvfp4_index_k_dequant, _lib.indexer_score_decode, _lib.indexer_score_prefill,
-           _lib.topk16_select):
+           _lib.topk16_select, _lib.mxfp8_e4m3_quantize):
     _f.restype = ctypes.c_int
 _lib.pagescore_strerror.argtypes = [ctypes.c_int]
 _lib.pagescore_strerror.restype = ctypes.c_char_p
@@ -190,6 +191,25 @@ def topk16_select(scores, width: int, out, valid_len=None, force_begin=None, for
         _ptr(force_begin), _ptr(force_end), _ptr(append_page), _ptr(out), out.stride(0),
         _stream(scores)))
     return out
+
+
+def mxfp8_e4m3_quantize(x, q, scales):
+    """MXFP8 quantization of ``x [rows, cols]`` bf16 into ``q [rows, >=cols]``
+    E4M3 bytes and ``scales [rows, >=cols/32]`` E8M0 bytes."""
+    _need(x, "x", (torch.bfloat16, torch.int16, torch.uint16))
+    _need(q, "q", _U8)
+    _need(scales, "scales", (torch.uint8,))
+    for name, t in (("x", x), ("q", q), ("scales", scales)):
+        if t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name} must be 2-D with unit column stride")
+    rows, cols = x.shape
+    if q.shape[0] < rows or q.shape[1] < cols or scales.shape[0] < rows or \
+            scales.shape[1] < cols // 32:
+        raise ValueError("q [rows, >=cols] and scales [rows, >=cols/32] expected")
+    _check("mxfp8_e4m3_quantize", _lib.mxfp8_e4m3_quantize(
+        _ptr(x), x.stride(0), int(rows), int(cols), _ptr(q), q.stride(0), _ptr(scales),
+        scales.stride(0), _stream(x)))
+    return q, scales
 
 
 def raw_library():

@@ -115,6 +115,20 @@ int topk16_select(const float *scores, int64_t row_stride, int32_t num_rows, int
                                                    out_stride, (hipStream_t)stream));
 }
 
+int mxfp8_e4m3_quantize(const uint16_t *x, int64_t x_stride, int32_t rows, int32_t cols, uint8_t *q,
+                        int64_t q_stride, uint8_t *scales, int64_t scale_stride, void *stream)
+{
+    if (rows < 0 || cols < 0 || cols % 32 != 0)
+        return PAGESCORE_EINVAL;
+    if (rows == 0 || cols == 0)
+        return PAGESCORE_OK;
+    if (!x || !aligned16(x) || x_stride < cols || x_stride % 8 != 0 || !q || !aligned16(q) ||
+        q_stride < cols || q_stride % 16 != 0 || !scales || scale_stride < cols / 32)
+        return PAGESCORE_EINVAL;
+    return launch_status(pagescore::launch_mxfp8_quant(x, x_stride, rows, cols, q, q_stride, scales,
+                                                        scale_stride, (hipStream_t)stream));
+}
+
 int pagescore_last_hip_error(void) { return g_last_hip_error; }
 
 const char *pagescore_strerror(int code)

@@ -146,6 +146,29 @@ def test_topk_host_checks(lib):
     assert _topk(lib, s=None) == EINVAL
 
 
+def _mx(lib, **kw):
+    a = dict(x=FAKE, xs=64, rows=4, cols=64, q=FAKE, qs=64, s=FAKE, ss=2)
+    a.update(kw)
+    f = lib.mxfp8_e4m3_quantize
+    f.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int64, P,
+                  ctypes.c_int64, P]
+    return f(a["x"], a["xs"], a["rows"], a["cols"], a["q"], a["qs"], a["s"], a["ss"], None)
+
+
+def test_mxfp8_host_checks(lib):
+    assert _mx(lib, rows=0) == 0
+    assert _mx(lib, cols=0) == 0
+    assert _mx(lib, rows=-1) == EINVAL
+    assert _mx(lib, cols=48) == EINVAL                   # not whole 32-element blocks
+    assert _mx(lib, x=ODD) == EINVAL
+    assert _mx(lib, xs=60) == EINVAL                     # stride below cols
+    assert _mx(lib, xs=68) == EINVAL                     # rows not 16-byte aligned
+    assert _mx(lib, q=ODD) == EINVAL
+    assert _mx(lib, qs=72) == EINVAL                     # q rows not 16-byte aligned
+    assert _mx(lib, ss=1) == EINVAL
+    assert _mx(lib, s=None) == EINVAL
+
+
 def test_strerror(lib):
     lib.pagescore_strerror.restype = ctypes.c_char_p
     assert lib.pagescore_strerror(0) == b"ok"

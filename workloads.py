@@ -222,6 +222,20 @@ def nvfp4_prefill(seed: int = 6) -> Nvfp4PrefillInputs:
     return nvfp4_prefill_inputs("nvfp4-prefill", seed, [2048], [65536])
 
 
+def mx_activations(seed: int, rows: int, cols: int, spread: float = 40.0) -> np.ndarray:
+    """bf16 bit patterns ``[rows, cols]`` (uint16) of attention-output-like
+    activations: N(0,1) values times a per-32-element-block magnitude
+    2^U(-spread, spread), so blocks span a wide dynamic range (the ROCm MXFP8
+    epilogue's tests use a wide magnitude range).  Rounded to bf16 by torch's
+    cast (input preparation only)."""
+    rng = _streams(seed)[_S_EXTRA]
+    base = rng.standard_normal((rows, cols)).astype(np.float32)
+    nb = (cols + 31) // 32
+    mag = np.exp2(rng.uniform(-spread, spread, size=(rows, nb))).astype(np.float32)
+    x = base * np.repeat(mag, 32, axis=1)[:, :cols]
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
 # ---------------------------------------------------------------------------
 # Score rows with injected special values, for the top-16 selection.
 # ---------------------------------------------------------------------------
