@@ -62,6 +62,8 @@ def lib():
             "ora_score_prefill_rows": (None, [P, P, P, P, I32, I32, P, I32, P]),
             "ora_rank_value": (D, [ctypes.c_float, ctypes.c_int]),
             "ora_topk16": (None, [P, I64, I32, I32, P, P, P, P, P, I64]),
+            "ora_causal_count": (I32, [I32, I32, I32, I32]),
+            "ora_score_prefill_ragged": (None, [P, P, P, P, I32, I32, P, P, P, I32, P, I64, P]),
             "ora_bf16_value": (D, [ctypes.c_int]),
             "ora_mx_block_scale": (ctypes.c_int, [P]),
             "ora_mxfp8_quantize": (None, [P, I64, I32, I32, P, I64, P, I64]),
@@ -202,6 +204,30 @@ def score_prefill_rows(q, q_scale, k, k_scale, rows):
                                  _p(_c(k_scale, np.float32)), H, N, _p(rows), len(rows),
                                  _p(out))
     return out
+
+
+def causal_count(q_len: int, k_len: int, i: int, width: int) -> int:
+    return lib().ora_causal_count(int(q_len), int(k_len), int(i), int(width))
+
+
+def score_prefill_ragged(q, q_scale, k, k_scale, q_start, k_start, k_len, width, scores=None,
+                         ld=None):
+    """Causal scores of a ragged batch: ``scores [T, ld >= width]`` float32
+    (columns >= width untouched; a new array is NaN there) and ``row_len [T]``."""
+    q = _c(q, np.uint8)
+    T, H = q.shape[0], q.shape[1]
+    k = _c(k, np.uint8)
+    q_start = _c(q_start, np.int32)
+    S = len(q_start) - 1
+    ld = width if ld is None else ld
+    if scores is None:
+        scores = np.full((T, ld), np.nan, dtype=np.float32)
+    row_len = np.full(T, -1, dtype=np.int32)
+    lib().ora_score_prefill_ragged(_p(q), _p(_c(q_scale, np.float32)), _p(k),
+                                   _p(_c(k_scale, np.float32)), H, S, _p(q_start),
+                                   _p(_c(k_start, np.int32)), _p(_c(k_len, np.int32)), int(width),
+                                   _p(scores), int(ld), _p(row_len))
+    return scores, row_len
 
 
 # ---------------------------------------------------------------------------

@@ -330,6 +330,50 @@ void ora_score_prefill_rows(const uint8_t *q, const float *q_scale,
             scores[(int64_t)i * N + n] = ora_score_prefill_one(q, q_scale, k, k_scale, H, rows[i], n);
 }
 
+/* [MOJO] a ragged batch with causal masking and the -inf tail fill (the
+ * module description names both as the follow-up slices of its prefill
+ * scorer; its Q is [total tokens, heads, depth] over a batch of sequences
+ * with paged K).
+ * READING: sequence s owns query rows [q_start[s], q_start[s+1]) and keys
+ * k[k_start[s] .. k_start[s] + k_len[s]); its queries are the last
+ * q_len = q_start[s+1] - q_start[s] tokens of its k_len-token context, so
+ * query i sits at position k_len - q_len + i and sees the keys at positions
+ * 0 .. k_len - q_len + i.  Row t = q_start[s] + i holds, for j < width,
+ * the score of key k_start[s] + j when j < count, else -inf, where
+ * count = clamp(k_len - q_len + i + 1, 0, min(k_len, width)); row_len[t] =
+ * count.  Columns >= width are not written. */
+int32_t ora_causal_count(int32_t q_len, int32_t k_len, int32_t i, int32_t width)
+{
+    int64_t c = (int64_t)k_len - q_len + i + 1;
+    int64_t hi = k_len < width ? k_len : width;
+    if (c > hi)
+        c = hi;
+    if (c < 0)
+        c = 0;
+    return (int32_t)c;
+}
+
+void ora_score_prefill_ragged(const uint8_t *q, const float *q_scale,
+                              const uint8_t *k, const float *k_scale, int32_t H,
+                              int32_t num_seqs, const int32_t *q_start,
+                              const int32_t *k_start, const int32_t *k_len,
+                              int32_t width, float *scores, int64_t ld, int32_t *row_len)
+{
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        int32_t q_len = q_start[s + 1] - q_start[s];
+        for (int32_t i = 0; i < q_len; ++i) {
+            int64_t t = (int64_t)q_start[s] + i;
+            int32_t count = ora_causal_count(q_len, k_len[s], i, width);
+            for (int32_t j = 0; j < width; ++j)
+                scores[t * ld + j] =
+                    j < count ? ora_score_prefill_one(q, q_scale, k, k_scale, H, t,
+                                                      (int64_t)k_start[s] + j)
+                              : -INFINITY;
+            row_len[t] = count;
+        }
+    }
+}
+
 /* ------------------------------------------------------------------------
  * Top-16.
  * ---------------------------------------------------------------------- */
