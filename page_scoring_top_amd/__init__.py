@@ -1,15 +1,17 @@
 """MI355X (gfx950) sparse-attention indexer path.
 
-Five calls, each a thin binding of the C ABI in include/pagescore.h:
+Six calls, each a thin binding of the C ABI in include/pagescore.h:
 
   nvfp4_index_k_dequant  -- gather NVFP4 index-K pages into contiguous E4M3 pages
   indexer_score_decode   -- fused NVFP4 dequant + per-page decode scores
   indexer_score_prefill  -- lightning-indexer scores summed over heads
+  indexer_score_prefill_ragged -- the same over a ragged batch, causally masked,
+                            rows filled with -inf past their visible keys
   topk16_select          -- exact top-16 column ids per score row
   mxfp8_e4m3_quantize    -- MXFP8 (E4M3 + E8M0) quantization of bf16 rows, the
                             step after the sparse attention
 
-The kernels are hand-written HIP in csrc/, built by page_scoring_top_amd.build.
+The kernels are hand-written HIP in csrc/, built by page_scoring_top_amd/build.py.
 """
 
 from ._binding import (  # noqa: F401
@@ -18,6 +20,7 @@ from ._binding import (  # noqa: F401
     PreparedCall,
     indexer_score_decode,
     indexer_score_prefill,
+    indexer_score_prefill_ragged,
     mxfp8_e4m3_quantize,
     nvfp4_index_k_dequant,
     prepare,
@@ -25,4 +28,5 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = ["nvfp4_index_k_dequant", "indexer_score_decode", "indexer_score_prefill",
+           "indexer_score_prefill_ragged",
            "topk16_select", "mxfp8_e4m3_quantize", "prepare", "PreparedCall", "PageScoreError", "LIB_PATH"]

@@ -18,7 +18,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagesco
 
 if not os.path.exists(_LIB_PATH):
     raise ImportError(
-        f"{_LIB_PATH} is missing: build it with `python -m page_scoring_top_amd.build` "
+        f"{_LIB_PATH} is missing: build it with `python page_scoring_top_amd/build.py` "
         "(or __graft_entry__.build()); the indexer path has no CPU fallback")
 
 _lib = ctypes.CDLL(_LIB_PATH)
@@ -30,8 +30,10 @@ _lib.indexer_score_decode.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P, _P, _I32
 _lib.indexer_score_prefill.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _P, _I64, _P]
 _lib.topk16_select.argtypes = [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _I64, _P]
 _lib.mxfp8_e4m3_quantize.argtypes = [_P, _I64, _I32, _I32, _P, _I64, _P, _I64, _P]
+_lib.indexer_score_prefill_ragged.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P,
+                                              _I32, _I32, _P, _I64, _P, _P]
 for _f in (_lib.nvfp4_index_k_dequant, _lib.indexer_score_decode, _lib.indexer_score_prefill,
-           _lib.topk16_select, _lib.mxfp8_e4m3_quantize):
+           _lib.topk16_select, _lib.mxfp8_e4m3_quantize, _lib.indexer_score_prefill_ragged):
     _f.restype = ctypes.c_int
 _lib.pagescore_strerror.argtypes = [ctypes.c_int]
 _lib.pagescore_strerror.restype = ctypes.c_char_p
@@ -163,6 +165,36 @@ def indexer_score_prefill(q, q_scale, k, k_scale, scores):
         raise ValueError("q [T,H,128], q_scale [T,H], k [N,128], k_scale [N] expected")
     _check("indexer_score_prefill", _lib.indexer_score_prefill(
         _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), T, H, N, _ptr(scores), scores.stride(0),
+        _stream(q)))
+    return scores
+
+
+def indexer_score_prefill_ragged(q, q_scale, k, k_scale, q_start, k_start, k_len, max_q: int,
+                                 width: int, scores, row_len=None):
+    """Causal lightning-indexer scores of a ragged batch into ``scores [T, >=width]``
+    (columns relative to each sequence's first key, -inf past a row's visible
+    keys) and the visible counts into ``row_len [T]``."""
+    _need(q, "q", _U8)
+    _need(q_scale, "q_scale", _F32)
+    _need(k, "k", _U8)
+    _need(k_scale, "k_scale", _F32)
+    for name, t in (("q_start", q_start), ("k_start", k_start), ("k_len", k_len),
+                    ("row_len", row_len)):
+        _need(t, name, _I32T)
+    _need(scores, "scores", _F32)
+    T, H = q.shape[0], q.shape[1]
+    N = k.shape[0]
+    S = q_start.numel() - 1
+    if not all(t.is_contiguous() for t in (q, q_scale, k, k_scale, q_start, k_start, k_len)):
+        raise ValueError("inputs must be contiguous")
+    if scores.dim() != 2 or scores.stride(1) != 1 or scores.shape[0] < T or scores.shape[1] < width:
+        raise ValueError("scores must be [T, >=width] with unit column stride")
+    if S < 0 or k_start.numel() < S or k_len.numel() < S or (row_len is not None and
+                                                             row_len.numel() < T):
+        raise ValueError("q_start [S+1], k_start [S], k_len [S], row_len [T] expected")
+    _check("indexer_score_prefill_ragged", _lib.indexer_score_prefill_ragged(
+        _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), T, H, N, S, _ptr(q_start), _ptr(k_start),
+        _ptr(k_len), int(max_q), int(width), _ptr(scores), scores.stride(0), _ptr(row_len),
         _stream(q)))
     return scores
 

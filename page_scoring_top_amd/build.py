@@ -1,6 +1,9 @@
 """Build libpagescore.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m page_scoring_top_amd.build
+    python page_scoring_top_amd/build.py
+
+(run by path: importing the package loads the library, which may not exist
+yet or may predate a new entry point)
 
 Every source under csrc/ is compiled by hipcc to an object, in parallel, and
 the objects are linked into page_scoring_top_amd/libpagescore.so.  Packed FP32

@@ -24,7 +24,7 @@ def declared_functions():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        pytest.fail("libpagescore.so is not built (python -m page_scoring_top_amd.build)")
+        pytest.fail("libpagescore.so is not built (python page_scoring_top_amd/build.py)")
     return ctypes.CDLL(LIB)
 
 
