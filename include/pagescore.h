@@ -156,6 +156,44 @@ int indexer_score_prefill(const uint8_t *q, const float *q_scale, const uint8_t 
                           float *scores, int64_t ld, void *stream);
 
 /*
+ * indexer_score_prefill_ragged -- the lightning-indexer scores of a ragged
+ * batch of sequences with causal masking and the -inf tail fill ([MOJO]
+ * module description: Q over all tokens of a batch, paged K, the mask and
+ * the fill as its follow-up steps).
+ *
+ * Sequence s owns query rows [q_start[s], q_start[s+1]) of q and keys
+ * k[k_start[s] .. k_start[s] + k_len[s]).  Its q_len queries are the last
+ * q_len tokens of its k_len-token context, so query i (row t = q_start[s]+i)
+ * sees count = clamp(k_len - q_len + i + 1, 0, min(k_len, width)) keys, and
+ *     scores[t, j] = score(q[t], k[k_start[s] + j])   for j < count
+ *     scores[t, j] = -inf                              for count <= j < width
+ * with the same score and relu as indexer_score_prefill; columns >= width
+ * are not written, and row_len[t] = count when row_len is given (the
+ * valid_len of topk16_select for the row).
+ *
+ *   q, q_scale, k, k_scale  as for indexer_score_prefill (T rows, N keys).
+ *   q_start   [num_seqs + 1] int32, non-decreasing row offsets.
+ *   k_start, k_len  [num_seqs] int32.
+ *   max_q     at least every sequence's q_len (rows past it are not
+ *             written).
+ *   scores    [T, ld] float32, ld >= width.
+ *   row_len   nullable [T] int32.
+ * 1 <= H <= PAGESCORE_RAGGED_MAX_HEADS and num_seqs <=
+ * PAGESCORE_RAGGED_MAX_SEQS, else PAGESCORE_EINVAL.  T, num_seqs or max_q
+ * == 0 returns PAGESCORE_OK with no launch.  Device-side, row offsets are
+ * clamped to [0, T] and a key slice leaving k[0, N) is cut to the part
+ * inside it.
+ */
+#define PAGESCORE_RAGGED_MAX_HEADS 64
+#define PAGESCORE_RAGGED_MAX_SEQS 65535
+int indexer_score_prefill_ragged(const uint8_t *q, const float *q_scale, const uint8_t *k,
+                                 const float *k_scale, int32_t T, int32_t H, int32_t N,
+                                 int32_t num_seqs, const int32_t *q_start,
+                                 const int32_t *k_start, const int32_t *k_len, int32_t max_q,
+                                 int32_t width, float *scores, int64_t ld, int32_t *row_len,
+                                 void *stream);
+
+/*
  * topk16_select -- exact top-16 column ids of each score row ([MSA] "Changes"
  * and "Behaviour changes vs f380d0e" for the order; [DECODE] module
  * description and _merge_kernel for the 15 + own-page row).

@@ -99,6 +99,25 @@ int indexer_score_prefill(const uint8_t *q, const float *q_scale, const uint8_t 
                                                          (hipStream_t)stream));
 }
 
+int indexer_score_prefill_ragged(const uint8_t *q, const float *q_scale, const uint8_t *k,
+                                 const float *k_scale, int32_t T, int32_t H, int32_t N,
+                                 int32_t num_seqs, const int32_t *q_start, const int32_t *k_start,
+                                 const int32_t *k_len, int32_t max_q, int32_t width, float *scores,
+                                 int64_t ld, int32_t *row_len, void *stream)
+{
+    if (T < 0 || N < 0 || H < 1 || H > PAGESCORE_RAGGED_MAX_HEADS || num_seqs < 0 ||
+        num_seqs > PAGESCORE_RAGGED_MAX_SEQS || max_q < 0 || width < 1)
+        return PAGESCORE_EINVAL;
+    if (T == 0 || num_seqs == 0 || max_q == 0)
+        return PAGESCORE_OK;
+    if (!q || !aligned16(q) || !q_scale || !k || !aligned16(k) || !k_scale || !q_start || !k_start ||
+        !k_len || !scores || ld < width)
+        return PAGESCORE_EINVAL;
+    return launch_status(pagescore::launch_score_prefill_ragged(
+        q, q_scale, k, k_scale, T, H, N, num_seqs, q_start, k_start, k_len, max_q, width, scores, ld,
+        row_len, (hipStream_t)stream));
+}
+
 int topk16_select(const float *scores, int64_t row_stride, int32_t num_rows, int32_t width,
                   const int32_t *valid_len, const int32_t *force_begin, const int32_t *force_end,
                   const int32_t *append_page, int32_t *out, int64_t out_stride, void *stream)

@@ -149,6 +149,15 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
 // dropped), so the loop body has no branches and the interleaving spans
 // whole chunks.
 // ---------------------------------------------------------------------------
+// Ragged causal batch description (unused by the dense launch).
+struct RaggedBatch {
+    const int32_t *q_start;   // [num_seqs + 1]
+    const int32_t *k_start;   // [num_seqs]
+    const int32_t *k_len;     // [num_seqs]
+    int32_t *row_len;         // [T] or null
+    int32_t width;            // score columns per row
+};
+
 constexpr int kH64Waves = 8;                                  // tokens per work-group
 constexpr int kChunkKeys = 128;
 constexpr int kChunkBufs = 3;
@@ -172,11 +181,19 @@ constexpr int64_t kPackMaxLd = 1 << 24;                       // 16 rows of scor
 // tile ht is then head i % 4 of token 8 ht + 2 (i / 4) + half, so the head
 // sum of a (token, key) score is four elements of one lane, and a lane
 // stores 4 kHT scores per tile.
-template <int kHT, bool kPack>
+// kCausal: a ragged batch of sequences (grid z), each query row masked
+// causally and its row filled with -inf past its visible keys.  Sequence s
+// owns query rows [q_start[s], q_start[s+1]) and keys k_start[s] ..
+// + k_len[s]; its queries are the last q_len tokens of its context, so
+// query i sees count(i) = clamp(k_len - q_len + i + 1, 0, min(k_len, width))
+// keys.  Score columns are relative to the sequence's first key; a
+// work-group computes only the key chunks some of its queries see and fills
+// the rest of its column range with -inf.
+template <int kHT, bool kPack, bool kCausal>
 __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel(
     const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
     const uint8_t *__restrict__ k, const float *__restrict__ k_scale, int32_t T, int32_t H,
-    int32_t N, int32_t keys_per_group, float *__restrict__ scores, int64_t ld)
+    int32_t N, int32_t keys_per_group, float *__restrict__ scores, int64_t ld, RaggedBatch rb)
 {
     __shared__ __align__(16) uint8_t kbuf[kChunkBufs][kChunkKeys * kKeyRowBytes];
     __shared__ float ks_lds[kChunkBufs][kChunkKeys];
@@ -186,12 +203,56 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
     const int col = lane & 31;
     const int half = lane >> 5;
     constexpr int kTokPerWave = kPack ? 8 * kHT : 1;
-    const int64_t t = ((int64_t)blockIdx.x * kH64Waves + wave) * kTokPerWave;
-    const bool tok_ok = t < T;
-    const int tok_rows = !tok_ok ? 0 : (T - t < kTokPerWave ? (int)(T - t) : kTokPerWave);
+    constexpr int kTokPerGroup = kH64Waves * kTokPerWave;
+    // Query rows [row0, row_end) and keys [0, klen) of k / k_scale from here
+    // on; the work-group's tokens start at row0 + tb and its columns are
+    // [kb, ke), of which [kb, kc) are computed.
+    int64_t row0 = 0, row_end = T;
+    int32_t klen = N, width = N;
+    if constexpr (kCausal) {
+        const int sq = blockIdx.z;
+        int64_t a0 = rb.q_start[sq], a1 = rb.q_start[sq + 1];
+        a0 = a0 < 0 ? 0 : (a0 > T ? T : a0);
+        a1 = a1 < a0 ? a0 : (a1 > T ? T : a1);
+        row0 = __builtin_amdgcn_readfirstlane((int32_t)a0);
+        row_end = __builtin_amdgcn_readfirstlane((int32_t)a1);
+        // Keys outside k[0, N) are never read: a sequence whose slice leaves
+        // the buffer is cut to the part inside it.
+        const int64_t k0 = rb.k_start[sq];
+        int64_t kl = rb.k_len[sq];
+        kl = (k0 < 0 || k0 > N) ? 0 : (kl > N - k0 ? N - k0 : (kl < 0 ? 0 : kl));
+        klen = __builtin_amdgcn_readfirstlane((int32_t)kl);
+        width = rb.width;
+        k += (k0 < 0 || k0 > N ? 0 : k0) * kDepth;
+        k_scale += (k0 < 0 || k0 > N ? 0 : k0);
+    }
+    const int q_len = (int)(row_end - row0);
+    const int tb = blockIdx.x * kTokPerGroup;
+    if (tb >= q_len)
+        return;
+    const int iw = tb + wave * kTokPerWave;                 // the wave's first query of the sequence
+    const int64_t t = row0 + iw;
+    const int tok_rows = iw >= q_len ? 0 : (q_len - iw < kTokPerWave ? q_len - iw : kTokPerWave);
+    const bool tok_ok = tok_rows > 0;
     const int kb = blockIdx.y * keys_per_group;
-    const int ke = kb + keys_per_group < N ? kb + keys_per_group : N;
-    const int chunks = (ke - kb + kChunkKeys - 1) / kChunkKeys;
+    const int ke = kb + keys_per_group < width ? kb + keys_per_group : width;
+    // Visible keys of query i of the sequence (all of them without the mask).
+    auto visible = [&](int i) {
+        if constexpr (!kCausal)
+            return klen;
+        const int64_t c = (int64_t)klen - q_len + i + 1;
+        const int hi = klen < width ? klen : width;
+        return (int)(c > hi ? hi : (c < 0 ? 0 : c));
+    };
+    int kc = ke;
+    if constexpr (kCausal) {
+        const int last = tb + kTokPerGroup < q_len ? tb + kTokPerGroup - 1 : q_len - 1;
+        const int cmax = visible(last);
+        kc = cmax < kb ? kb : (cmax < ke ? cmax : ke);
+        if (blockIdx.y == 0 && rb.row_len != nullptr && lane < tok_rows)
+            rb.row_len[t + lane] = visible(iw + lane);
+    }
+    const int chunks = (kc - kb + kChunkKeys - 1) / kChunkKeys;
 
     // Query rows as f16 A operands: head 32 ht + col, depth 16 st + 8 half
     // .. +8 (zero past H, and for a token past T); kHT head tiles of 32.
@@ -232,9 +293,9 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
         float ks;
     };
     auto load_chunk = [&](int c, Raw &r) {
-        // Keys [kb + 128 c, ke): a chunk past the range has no records.
+        // Keys [kb + 128 c, kc): a chunk past the range has no records.
         const int base = kb + c * kChunkKeys;
-        const int live = c < chunks ? (ke - base < kChunkKeys ? ke - base : kChunkKeys) : 0;
+        const int live = c < chunks ? (kc - base < kChunkKeys ? kc - base : kChunkKeys) : 0;
         const __amdgpu_buffer_rsrc_t kr = uniform_rsrc(k + (int64_t)(c < chunks ? base : 0) * kDepth,
                                                        (uint32_t)live * kDepth);
         const __amdgpu_buffer_rsrc_t sr = uniform_rsrc(k_scale + (c < chunks ? base : 0),
@@ -265,12 +326,18 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
         tok_ok ? (uint32_t)(((int64_t)(tok_rows - 1) * ld + (ke - kb)) * 4) : 0u);
     const int key_count = ke - kb;
     uint32_t row_off[kPack ? 4 * kHT : 1];
+    // Causal: a store of column kb + n writes -inf unless n < vis_rel (the
+    // row's visible keys relative to kb).
+    int vis_rel[kPack ? 4 * kHT : 1];
     if constexpr (kPack) {
 #pragma unroll
         for (int g = 0; g < 4 * kHT; ++g) {
             const int u = 8 * (g / 4) + 2 * (g % 4) + half;
             row_off[g] = u < tok_rows ? (uint32_t)(u * ld * 4) : kDropped;
+            vis_rel[g] = visible(iw + u) - kb;
         }
+    } else {
+        vis_rel[0] = visible(iw) - kb;
     }
 
     // The drain of a tile's accumulators is cut into 8 kHT slices, one per
@@ -317,9 +384,13 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
             const uint32_t key_off = (n_rel >= 0 && n < key_count) ? (uint32_t)n * 4u : kKeyDropped;
             const float hks = 0.5f * ks;
 #pragma unroll
-            for (int g = 0; g < kParts; ++g)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hks * part[g]), out,
-                                                      row_off[g] + key_off, 0, kStreamingStore);
+            for (int g = 0; g < kParts; ++g) {
+                float v = hks * part[g];
+                if constexpr (kCausal)
+                    v = n < vis_rel[g] ? v : -INFINITY;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), out, row_off[g] + key_off, 0,
+                                                      kStreamingStore);
+            }
             return;
         }
         const float sum = (part[0] + part[1]) + (part[2] + part[3]);
@@ -327,7 +398,10 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
                                                          false, false);
         const float total = sum + __uint_as_float(sw[1]);   // lanes 0..31: the other half's sum
         const uint32_t off = (half == 0 && n_rel >= 0) ? (uint32_t)(n_rel + col) * 4u : kDropped;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ks * (0.5f * total)), out, off, 0, 0);
+        float v = ks * (0.5f * total);
+        if constexpr (kCausal)
+            v = n_rel + col < vis_rel[0] ? v : -INFINITY;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), out, off, 0, 0);
     };
 
     // B operand of tile kt, K step st of the chunk in buffer buf.
@@ -414,6 +488,16 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
     for (int m = 0; m < 8 * kHT; ++m)
         drain_slice(acc[(kTilesPerChunk - 1) & 1], m);
     drain_tail(ks_prev, n_prev);
+    if constexpr (kCausal) {
+        // The -inf tail past the computed chunks: columns [kb + 128 chunks, ke)
+        // of the wave's rows.
+        const int fill0 = chunks * kChunkKeys;
+        for (int u = 0; u < tok_rows; ++u)
+            for (int n = fill0 + lane; n < ke - kb; n += kWave)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), out,
+                                                      (uint32_t)(u * ld * 4) + (uint32_t)n * 4u, 0,
+                                                      kStreamingStore);
+    }
 }
 
 }  // namespace
@@ -421,49 +505,76 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
 static_assert(kPrefillMaxHeads * ((kRowHalves * 2) + 4) <= kLdsBytes,
               "one token of the largest head count must fit the work-group's LDS");
 
+namespace {
+
+// Launch of the small-head kernel over `token_groups` x key splits x
+// `num_seqs` work-groups, with columns [0, width) split in whole chunks of
+// 128 keys (at most 2^20 per work-group) so the grid holds about one
+// work-group per compute unit.
+template <bool kCausal>
+hipError_t launch_h64(const uint8_t *q, const float *q_scale, const uint8_t *k, const float *k_scale,
+                      int32_t T, int32_t H, int32_t N, float *scores, int64_t ld, int64_t max_q,
+                      int32_t width, int32_t num_seqs, const RaggedBatch &rb, hipStream_t stream)
+{
+    // Up to four heads, 16 tokens per wave (8 for a short prefill); one
+    // token per wave otherwise.  Eight waves per work-group.
+    const bool pack = H <= kPackHeads && ld <= kPackMaxLd;
+    const int pack_tiles = max_q > 8 * kH64Waves ? 2 : 1;
+    const int64_t tokens_per_group = (int64_t)kH64Waves * (pack ? 8 * pack_tiles : 1);
+    const int64_t groups = (max_q + tokens_per_group - 1) / tokens_per_group;
+    if (groups > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    const int64_t busy = ((int64_t)T + tokens_per_group - 1) / tokens_per_group + num_seqs - 1;
+    const int64_t chunks = ((int64_t)width + kChunkKeys - 1) / kChunkKeys;
+    int64_t splits = (256 + busy - 1) / busy;
+    const int64_t min_splits = ((int64_t)width + kMaxKeysPerGroup - 1) / kMaxKeysPerGroup;
+    splits = splits < min_splits ? min_splits : splits;
+    splits = splits < 1 ? 1 : (splits > chunks ? chunks : splits);
+    const int64_t keys_per_group = ((chunks + splits - 1) / splits) * kChunkKeys;
+    splits = ((int64_t)width + keys_per_group - 1) / keys_per_group;
+    if (splits > 65535)
+        return hipErrorInvalidValue;
+    const dim3 grid((uint32_t)groups, (uint32_t)splits, (uint32_t)num_seqs), block(kH64Waves * kWave);
+    // Packed tokens up to four heads; otherwise one 32-head MFMA tile up to
+    // 32 heads, two up to 64.
+    if (pack && pack_tiles == 2)
+        hipLaunchKernelGGL((score_prefill_h64_kernel<2, true, kCausal>), grid, block, 0, stream, q,
+                           q_scale, k, k_scale, T, H, N, (int32_t)keys_per_group, scores, ld, rb);
+    else if (pack)
+        hipLaunchKernelGGL((score_prefill_h64_kernel<1, true, kCausal>), grid, block, 0, stream, q,
+                           q_scale, k, k_scale, T, H, N, (int32_t)keys_per_group, scores, ld, rb);
+    else if (H <= 32)
+        hipLaunchKernelGGL((score_prefill_h64_kernel<1, false, kCausal>), grid, block, 0, stream, q,
+                           q_scale, k, k_scale, T, H, N, (int32_t)keys_per_group, scores, ld, rb);
+    else
+        hipLaunchKernelGGL((score_prefill_h64_kernel<2, false, kCausal>), grid, block, 0, stream, q,
+                           q_scale, k, k_scale, T, H, N, (int32_t)keys_per_group, scores, ld, rb);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_score_prefill_ragged(const uint8_t *q, const float *q_scale, const uint8_t *k,
+                                       const float *k_scale, int32_t T, int32_t H, int32_t N,
+                                       int32_t num_seqs, const int32_t *q_start,
+                                       const int32_t *k_start, const int32_t *k_len, int32_t max_q,
+                                       int32_t width, float *scores, int64_t ld, int32_t *row_len,
+                                       hipStream_t stream)
+{
+    if (H > kSmallHeads || num_seqs > 65535)
+        return hipErrorInvalidValue;
+    const RaggedBatch rb{q_start, k_start, k_len, row_len, width};
+    return launch_h64<true>(q, q_scale, k, k_scale, T, H, N, scores, ld, max_q, width, num_seqs, rb,
+                            stream);
+}
+
 hipError_t launch_score_prefill(const uint8_t *q, const float *q_scale, const uint8_t *k,
                                 const float *k_scale, int32_t T, int32_t H, int32_t N,
                                 float *scores, int64_t ld, hipStream_t stream)
 {
-    if (H <= kSmallHeads) {
-        // One token per wave (eight packed tokens up to four heads), eight
-        // waves per work-group (one work-group per compute unit fits).  The
-        // keys are split so the grid holds about one work-group per compute
-        // unit, in whole chunks of 128 keys and at most 2^20 keys per
-        // work-group.
-        // Up to four heads, 16 tokens per wave (8 for a short prefill).
-        const bool pack = H <= kPackHeads && ld <= kPackMaxLd;
-        const int pack_tiles = T > 8 * kH64Waves ? 2 : 1;
-        const int64_t tokens_per_group = (int64_t)kH64Waves * (pack ? 8 * pack_tiles : 1);
-        const int64_t groups = ((int64_t)T + tokens_per_group - 1) / tokens_per_group;
-        if (groups > 0x7FFFFFFF)
-            return hipErrorInvalidValue;
-        const int64_t chunks = ((int64_t)N + kChunkKeys - 1) / kChunkKeys;
-        int64_t splits = (256 + groups - 1) / groups;
-        const int64_t min_splits = ((int64_t)N + kMaxKeysPerGroup - 1) / kMaxKeysPerGroup;
-        splits = splits < min_splits ? min_splits : splits;
-        splits = splits < 1 ? 1 : (splits > chunks ? chunks : splits);
-        const int64_t keys_per_group = ((chunks + splits - 1) / splits) * kChunkKeys;
-        splits = ((int64_t)N + keys_per_group - 1) / keys_per_group;
-        if (splits > 65535)
-            return hipErrorInvalidValue;
-        const dim3 grid((uint32_t)groups, (uint32_t)splits), block(kH64Waves * kWave);
-        // Packed tokens up to four heads; otherwise one 32-head MFMA tile up
-        // to 32 heads, two up to 64.
-        if (pack && pack_tiles == 2)
-            hipLaunchKernelGGL((score_prefill_h64_kernel<2, true>), grid, block, 0, stream, q, q_scale,
-                               k, k_scale, T, H, N, (int32_t)keys_per_group, scores, ld);
-        else if (pack)
-            hipLaunchKernelGGL((score_prefill_h64_kernel<1, true>), grid, block, 0, stream, q, q_scale,
-                               k, k_scale, T, H, N, (int32_t)keys_per_group, scores, ld);
-        else if (H <= 32)
-            hipLaunchKernelGGL((score_prefill_h64_kernel<1, false>), grid, block, 0, stream, q, q_scale,
-                               k, k_scale, T, H, N, (int32_t)keys_per_group, scores, ld);
-        else
-            hipLaunchKernelGGL((score_prefill_h64_kernel<2, false>), grid, block, 0, stream, q, q_scale,
-                               k, k_scale, T, H, N, (int32_t)keys_per_group, scores, ld);
-        return hipGetLastError();
-    }
+    if (H <= kSmallHeads)
+        return launch_h64<false>(q, q_scale, k, k_scale, T, H, N, scores, ld, T, N, 1, RaggedBatch{},
+                                 stream);
     const int hp = (H + 31) & ~31;
     const size_t per_token = (size_t)hp * (kRowHalves * 2 + 4);
     int tb = (int)(kLdsBytes / per_token);

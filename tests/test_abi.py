@@ -146,6 +146,31 @@ def test_topk_host_checks(lib):
     assert _topk(lib, s=None) == EINVAL
 
 
+def _ragged(lib, **kw):
+    a = dict(q=FAKE, qs=FAKE, k=FAKE, ks=FAKE, T=8, H=4, N=100, S=2, q_start=FAKE, k_start=FAKE,
+             k_len=FAKE, max_q=8, W=100, s=FAKE, ld=100, row_len=None)
+    a.update(kw)
+    f = lib.indexer_score_prefill_ragged
+    I32 = ctypes.c_int32
+    f.argtypes = [P, P, P, P, I32, I32, I32, I32, P, P, P, I32, I32, P, ctypes.c_int64, P, P]
+    return f(a["q"], a["qs"], a["k"], a["ks"], a["T"], a["H"], a["N"], a["S"], a["q_start"],
+             a["k_start"], a["k_len"], a["max_q"], a["W"], a["s"], a["ld"], a["row_len"], None)
+
+
+def test_ragged_prefill_host_checks(lib):
+    assert _ragged(lib, T=0) == 0
+    assert _ragged(lib, S=0) == 0
+    assert _ragged(lib, max_q=0) == 0
+    assert _ragged(lib, H=65) == EINVAL                 # beyond the small-head kernel
+    assert _ragged(lib, H=0) == EINVAL
+    assert _ragged(lib, S=65536) == EINVAL
+    assert _ragged(lib, W=0) == EINVAL
+    assert _ragged(lib, ld=99) == EINVAL
+    assert _ragged(lib, q=ODD) == EINVAL
+    assert _ragged(lib, k_len=None) == EINVAL
+    assert _ragged(lib, q_start=None) == EINVAL
+
+
 def _mx(lib, **kw):
     a = dict(x=FAKE, xs=64, rows=4, cols=64, q=FAKE, qs=64, s=FAKE, ss=2)
     a.update(kw)

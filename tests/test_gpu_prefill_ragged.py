@@ -1,0 +1,105 @@
+"""GPU parity of indexer_score_prefill_ragged against the oracle (Modular page
+"sparse_index_fp8_sm100", module description: a ragged batch, causal
+masking, the -inf tail fill): visible scores within
+|gpu - oracle| <= 1e-6 + 1e-5 |oracle|, every masked column exactly -inf,
+row_len exact, nothing written at or past the width, and the top-16 of each
+row (valid_len = row_len) equal to the oracle's selection over the GPU's own
+scores."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import CANARY_F32, CANARY_I32, announce, assert_scores_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def ragged_batch(seed, q_lens, k_lens, H, gap=5):
+    q_start = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    k_start = np.zeros(len(k_lens), np.int32)
+    off = 3
+    for s, kl in enumerate(k_lens):
+        k_start[s] = off
+        off += kl + gap
+    T = int(q_start[-1])
+    p = workloads.prefill_inputs("ragged", seed, T, H, off)
+    return p, q_start, k_start, np.asarray(k_lens, np.int32)
+
+
+def run(p, q_start, k_start, k_len, width, ld, max_q=None):
+    import page_scoring_top_amd as ps
+    T = p.q.shape[0]
+    scores = torch.full((T, ld), float(CANARY_F32), dtype=torch.float32, device="cuda")
+    row_len = torch.full((T,), int(CANARY_I32), dtype=torch.int32, device="cuda")
+    max_q = int(np.diff(q_start).max()) if max_q is None else max_q
+    ps.indexer_score_prefill_ragged(dev(p.q), dev(p.q_scale), dev(p.k), dev(p.k_scale),
+                                    dev(q_start), dev(k_start), dev(k_len), max_q, width, scores,
+                                    row_len)
+    ids = torch.full((T, 16), int(CANARY_I32), dtype=torch.int32, device="cuda")
+    ps.topk16_select(scores, width, ids, valid_len=row_len)
+    return host(scores), host(row_len), host(ids)
+
+
+CASES = [
+    # (q_lens, k_lens): single tokens, a chunk equal to its context (lower
+    # triangle), long contexts split over key groups, an empty sequence, a
+    # chunk longer than its context, ragged token groups.
+    ([1, 37, 130, 5, 0, 64, 300, 10], [1, 1000, 130, 3000, 200, 64, 2000, 3]),
+    ([129], [129]),
+    ([3, 2], [5000, 7]),
+]
+
+
+@pytest.mark.parametrize("H", [4, 20, 64])
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_ragged_batch(H, case):
+    q_lens, k_lens = CASES[case]
+    p, q_start, k_start, k_len = ragged_batch(31 * case + H, q_lens, k_lens, H)
+    width = max(k_lens) + 2
+    announce(f"ragged prefill H={H} q_lens={q_lens} k_lens={k_lens}")
+    got, row_len, ids = run(p, q_start, k_start, k_len, width, width + 3)
+    want, want_len = oracle.score_prefill_ragged(p.q, p.q_scale, p.k, p.k_scale, q_start, k_start,
+                                                 k_len, width)
+    assert np.array_equal(row_len, want_len), "row_len differs"
+    assert_scores_close(got[:, :width], want, f"H={H} case {case}")
+    assert (got[:, width:].view(np.int32) == CANARY_F32.view(np.int32)).all(), "write past width"
+    want_ids = oracle.topk16(got[:, :width], valid_len=want_len)
+    assert np.array_equal(ids, want_ids), "top-16 differs"
+
+
+def test_width_below_context():
+    """Rows are cut at the width: counts clamp to it and nothing is written
+    past it."""
+    p, q_start, k_start, k_len = ragged_batch(7, [40, 8], [900, 50], 4)
+    width = 300
+    announce("ragged prefill width below context")
+    got, row_len, _ = run(p, q_start, k_start, k_len, width, width + 1)
+    want, want_len = oracle.score_prefill_ragged(p.q, p.q_scale, p.k, p.k_scale, q_start, k_start,
+                                                 k_len, width)
+    assert np.array_equal(row_len, want_len)
+    assert_scores_close(got[:, :width], want, "width below context")
+    assert (got[:, width:].view(np.int32) == CANARY_F32.view(np.int32)).all()
+
+
+def test_big_batch_sampled_rows():
+    """Four sequences of 512 queries with 4,096 .. 16,384-token contexts and
+    64 heads (2,048 rows x 16,384 columns, the benchmark's launch
+    configuration): sampled full rows against the oracle."""
+    d = workloads.ragged_prefill()
+    announce("ragged prefill 4 x 512 x 64 heads, contexts 4096..16384")
+    got, row_len, _ = run(d.p, d.q_start, d.k_start, d.k_len, d.width, d.width)
+    rows = [0, 1, 511, 512, 1000, 1535, 1536, 2047]
+    for t in rows:
+        s = int(np.searchsorted(d.q_start, t, side="right") - 1)
+        i = t - int(d.q_start[s])
+        q_len = int(d.q_start[s + 1] - d.q_start[s])
+        c = oracle.causal_count(q_len, int(d.k_len[s]), i, d.width)
+        assert row_len[t] == c
+        k0 = int(d.k_start[s])
+        want = oracle.score_prefill_rows(d.p.q, d.p.q_scale, d.p.k[k0:k0 + c], d.p.k_scale[k0:k0 + c],
+                                         [t])[0]
+        assert_scores_close(got[t, :c], want, f"row {t}")
+        assert np.all(np.isneginf(got[t, c:]))

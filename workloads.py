@@ -222,6 +222,32 @@ def nvfp4_prefill(seed: int = 6) -> Nvfp4PrefillInputs:
     return nvfp4_prefill_inputs("nvfp4-prefill", seed, [2048], [65536])
 
 
+@dataclasses.dataclass
+class RaggedPrefillInputs:
+    p: PrefillInputs          # q [T, H, 128], keys of all sequences back to back
+    q_start: np.ndarray       # [S + 1] int32
+    k_start: np.ndarray       # [S] int32
+    k_len: np.ndarray         # [S] int32
+    width: int
+
+
+def ragged_prefill_inputs(name: str, seed: int, q_lens, k_lens, H: int) -> RaggedPrefillInputs:
+    """A ragged causal prefill batch: sequence s has q_lens[s] queries (the
+    last tokens of its context) and k_lens[s] keys, stored back to back."""
+    q_start = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    k_start = np.concatenate([[0], np.cumsum(k_lens)[:-1]]).astype(np.int32)
+    p = prefill_inputs(name, seed, int(q_start[-1]), H, int(np.sum(k_lens)))
+    return RaggedPrefillInputs(p, q_start, k_start, np.asarray(k_lens, np.int32),
+                               int(max(k_lens)))
+
+
+def ragged_prefill(seed: int = 8) -> RaggedPrefillInputs:
+    """Four sequences, each a 512-token prefill chunk at the end of a 4,096 /
+    8,192 / 12,288 / 16,384-token context, 64 heads: 2,048 query rows against
+    40,960 keys, row width 16,384."""
+    return ragged_prefill_inputs("ragged-prefill", seed, [512] * 4, [4096, 8192, 12288, 16384], 64)
+
+
 def mx_activations(seed: int, rows: int, cols: int, spread: float = 40.0) -> np.ndarray:
     """bf16 bit patterns ``[rows, cols]`` (uint16) of attention-output-like
     activations: N(0,1) values times a per-32-element-block magnitude
