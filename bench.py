@@ -23,6 +23,7 @@ bounded sample of the same workload.
   python bench.py --workload dequant # NVFP4 gather-dequantize of the decode pages
   python bench.py --workload nvfp4-prefill  # NVFP4 pages gathered, scored (4 heads), top-16
   python bench.py --workload mxfp8   # MXFP8 quantization of the attention output
+  python bench.py --workload ragged-prefill  # causal ragged prefill (4 sequences, 64 heads)
 """
 
 from __future__ import annotations
@@ -80,7 +81,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
     ap.add_argument("--workload", choices=("decode", "prefill", "dequant", "nvfp4-prefill",
-                                           "mxfp8"),
+                                           "mxfp8", "ragged-prefill"),
                     default="decode")
     return ap.parse_args()
 
@@ -171,6 +172,103 @@ def bench_prefill(args):
             "kind": "oracle",
             "sample": f"oracle prefill scores of {n} full rows ({t_rows:.2f} s), scaled to {T} rows; "
                       f"top-16 not included; step estimate {cpu_step:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
+def bench_ragged_prefill(args):
+    """Ragged causal prefill: four sequences, each a 512-token chunk at the
+    end of a 4,096 / 8,192 / 12,288 / 16,384-token context, 64 heads; scores
+    masked causally with the -inf tail fill over a 16,384-column row, then
+    the top-16 of every row over its visible keys."""
+    import numpy as np
+    import torch
+
+    import page_scoring_top_amd as ps
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    d = workloads.ragged_prefill()
+    T, H = d.p.q.shape[0], d.p.q.shape[1]
+    W = d.width
+    q = torch.from_numpy(d.p.q).to(dev)
+    qs = torch.from_numpy(d.p.q_scale).to(dev)
+    k = torch.from_numpy(d.p.k).to(dev)
+    ks = torch.from_numpy(d.p.k_scale).to(dev)
+    q_start = torch.from_numpy(d.q_start).to(dev)
+    k_start = torch.from_numpy(d.k_start).to(dev)
+    k_len = torch.from_numpy(d.k_len).to(dev)
+    max_q = int(np.diff(d.q_start).max())
+    scores = torch.empty((T, W), dtype=torch.float32, device=dev)
+    row_len = torch.empty((T,), dtype=torch.int32, device=dev)
+    out = torch.empty((T, 16), dtype=torch.int32, device=dev)
+    score_call = ps.prepare(ps.indexer_score_prefill_ragged, q, qs, k, ks, q_start, k_start, k_len,
+                            max_q, W, scores, row_len)
+    topk_call = ps.prepare(ps.topk16_select, scores, W, out, valid_len=row_len)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        score_call()
+        topk_call()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    ms_per_step = timed(torch, stream, step, K)
+    score_ms = timed(torch, stream, lambda i: score_call(), K)
+    topk_ms = timed(torch, stream, lambda i: topk_call(), K)
+    # Visible (query, key) pairs: sequence s's query i sees k_len - q_len + i + 1 keys.
+    pairs = 0
+    for s in range(len(d.k_len)):
+        ql = int(d.q_start[s + 1] - d.q_start[s])
+        kl = int(d.k_len[s])
+        pairs += sum(min(max(kl - ql + i + 1, 0), min(kl, W)) for i in range(ql))
+    flops = 2.0 * pairs * H * 128
+    achieved = flops / (score_ms * 1e-3) / 1e12
+    result = {
+        "metric": "ragged causal lightning-indexer prefill TFLOP/s (visible pairs) + top-16",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "e4m3 values as f16, f32 accumulate", "data": "synthetic",
+        "config": {"workload": "ragged causal prefill: 4 sequences x 512 query tokens x 64 heads "
+                               "at 4,096-16,384-token contexts, rows of 16,384 columns with the "
+                               "-inf tail fill, then top-16 of 2,048 rows",
+                   "tokens": T, "heads": H, "width": W, "visible_pairs": pairs,
+                   "parallelism": "single GPU"},
+        "kernels_us": {"indexer_score_prefill_ragged": round(score_ms * 1e3, 3),
+                       "topk16_select": round(topk_ms * 1e3, 3)},
+        "roofline": {"bound": "mfma", "kernel": "indexer_score_prefill_ragged",
+                     "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops_per_launch": flops},
+    }
+    if not args.no_cpu:
+        import oracle
+        t0 = time.perf_counter()
+        n = 0
+        order = [int(d.q_start[s]) + 3 * n_ % 512 for n_ in range(1000) for s in range(4)]
+        done_pairs = 0
+        while n < len(order) and time.perf_counter() - t0 < args.cpu_seconds:
+            t = order[n]
+            s = int(np.searchsorted(d.q_start, t, side="right") - 1)
+            i = t - int(d.q_start[s])
+            c = oracle.causal_count(int(d.q_start[s + 1] - d.q_start[s]), int(d.k_len[s]), i, W)
+            k0 = int(d.k_start[s])
+            oracle.score_prefill_rows(d.p.q, d.p.q_scale, d.p.k[k0:k0 + c], d.p.k_scale[k0:k0 + c],
+                                      [t])
+            done_pairs += c
+            n += 1
+        t_rows = time.perf_counter() - t0
+        cpu_step = t_rows * pairs / max(done_pairs, 1)
+        result["cpu_baseline"] = {
+            "value": round(flops / cpu_step / 1e12, 9), "unit": "TFLOP/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"oracle scores of {n} full visible rows ({done_pairs} pairs, {t_rows:.2f} s) "
+                      f"spread over the four sequences, scaled to {pairs} pairs; top-16 not "
+                      f"included; step estimate {cpu_step:.1f} s"}
     print(json.dumps(result), flush=True)
 
 
@@ -448,6 +546,8 @@ def main():
         return bench_nvfp4_prefill(args)
     if args.workload == "mxfp8":
         return bench_mxfp8(args)
+    if args.workload == "ragged-prefill":
+        return bench_ragged_prefill(args)
 
     import numpy as np
 

@@ -149,6 +149,8 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
 // dropped), so the loop body has no branches and the interleaving spans
 // whole chunks.
 // ---------------------------------------------------------------------------
+constexpr int64_t kCausalTargetGroups = 1024;
+
 // Ragged causal batch description (unused by the dense launch).
 struct RaggedBatch {
     const int32_t *q_start;   // [num_seqs + 1]
@@ -519,6 +521,12 @@ hipError_t launch_h64(const uint8_t *q, const float *q_scale, const uint8_t *k, 
     // Up to four heads, 16 tokens per wave (8 for a short prefill); one
     // token per wave otherwise.  Eight waves per work-group.
     const bool pack = H <= kPackHeads && ld <= kPackMaxLd;
+    // Dense work is even, so about one work-group per compute unit.  Causal
+    // rows see different key counts: the one-token path oversubscribes the
+    // grid four times and lets the hardware balance it (measured 11% faster
+    // at 4 x 512 queries over 4K-16K keys); the packed path, whose work per
+    // key is small, keeps one work-group per compute unit.
+    const int64_t target_groups = (kCausal && !pack) ? kCausalTargetGroups : 256;
     const int pack_tiles = max_q > 8 * kH64Waves ? 2 : 1;
     const int64_t tokens_per_group = (int64_t)kH64Waves * (pack ? 8 * pack_tiles : 1);
     const int64_t groups = (max_q + tokens_per_group - 1) / tokens_per_group;
@@ -526,7 +534,7 @@ hipError_t launch_h64(const uint8_t *q, const float *q_scale, const uint8_t *k, 
         return hipErrorInvalidValue;
     const int64_t busy = ((int64_t)T + tokens_per_group - 1) / tokens_per_group + num_seqs - 1;
     const int64_t chunks = ((int64_t)width + kChunkKeys - 1) / kChunkKeys;
-    int64_t splits = (256 + busy - 1) / busy;
+    int64_t splits = (target_groups + busy - 1) / busy;
     const int64_t min_splits = ((int64_t)width + kMaxKeysPerGroup - 1) / kMaxKeysPerGroup;
     splits = splits < min_splits ? min_splits : splits;
     splits = splits < 1 ? 1 : (splits > chunks ? chunks : splits);
