@@ -41,14 +41,36 @@ sys.path.insert(0, ROOT)
 METRIC = "index-K GB/s scored (frac of HBM peak) + top-16 rows/s, 500K-token decode"
 HBM_PEAK_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "score_decode_long_counters.txt")
-SCORE_SOURCES = ["csrc/score_decode.hip", "csrc/device_common.hpp", "csrc/nvfp4_lut.hpp", "build.py"]
+SCORE_SOURCES = ["csrc/score_decode.hip", "csrc/device_common.hpp", "csrc/nvfp4_lut.hpp"]
+
+
+def _score_compile_flags():
+    """hipcc flags of csrc/score_decode.hip from page_scoring_top_amd/build.py
+    (loaded by path), without the machine-specific include paths."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_pagescore_build", os.path.join(ROOT, "page_scoring_top_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    flags = mod.common_flags() + mod.FILE_FLAGS.get("score_decode.hip", [])
+    out, skip = [], False
+    for f in flags:
+        if skip:
+            skip = False
+        elif f == "-I":
+            skip = True
+        else:
+            out.append(f)
+    return out
 
 
 def kernel_source_hash() -> str:
+    """Hash of the decode score kernel's sources and compile flags."""
     h = hashlib.sha256()
     for f in SCORE_SOURCES:
         with open(os.path.join(ROOT, "page_scoring_top_amd", f), "rb") as fh:
             h.update(fh.read())
+    h.update(" ".join(_score_compile_flags()).encode())
     return h.hexdigest()[:16]
 
 
