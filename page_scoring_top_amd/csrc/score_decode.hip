@@ -333,7 +333,9 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
     const int per = total / kXcds, extra = total % kXcds;
     const int logical = xcd < extra ? xcd * (per + 1) + slot : extra * (per + 1) + (xcd - extra) * per + slot;
     const int b = logical / gx;
-    const int j0 = ((logical % gx) * kWavesPerBlock + wave) * chunk;
+    // The run [j0, j1) is uniform; read through readfirstlane, the per-page
+    // bounds and page addresses stay in scalar registers.
+    const int j0 = __builtin_amdgcn_readfirstlane(((logical % gx) * kWavesPerBlock + wave) * chunk);
     uint8_t *stage = scale_stage[wave];
 
     // First round of loads, all independent: the request's length, the run's
@@ -350,7 +352,7 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
     load_request_raw(qraw, q, q_scale, qlen, b, lane, m, g);
 
     const int np = pages_scored(seq, width);
-    const int j1 = j0 + chunk < np ? j0 + chunk : np;
+    const int j1 = __builtin_amdgcn_readfirstlane(j0 + chunk < np ? j0 + chunk : np);
     // A work-group past the request's last page leaves as soon as the length
     // is in (the first work-group of a request stays: it writes row_own).
     // Ragged batches launch many such groups.
@@ -361,10 +363,12 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
     // (such a page is not scored).  The id is read with v_readlane, so the
     // page base is a scalar and every load uses it with a constant per-lane
     // offset.
+    // Page ids are 32-bit, so the bound is compared in 32 bits (scalar ALU).
+    const int32_t nb32 = num_blocks > 0x7FFFFFFF ? 0x7FFFFFFF : (int32_t)num_blocks;
     auto page_src = [&](int j, bool &ok) -> __amdgpu_buffer_rsrc_t {
-        const int64_t id = __builtin_amdgcn_readlane(id_lane, j - j0);
-        ok = j < j1 && id >= 0 && id < num_blocks;
-        return page_rsrc(kv + (ok ? id : 0) * page_stride, ok);
+        const int32_t id = __builtin_amdgcn_readlane(id_lane, j - j0);
+        ok = j < j1 && id >= 0 && id < nb32;
+        return page_rsrc(kv + (int64_t)(ok ? id : 0) * page_stride, ok);
     };
     // The first page is requested without a branch (an empty run gets an
     // empty descriptor): after a conditional load the compiler could not
