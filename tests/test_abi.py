@@ -28,10 +28,10 @@ def lib():
     return ctypes.CDLL(LIB)
 
 
-def test_header_declares_the_four_calls():
+def test_header_declares_every_call():
     fns = declared_functions()
     for name in ("nvfp4_index_k_dequant", "indexer_score_decode", "indexer_score_prefill",
-                 "topk16_select"):
+                 "indexer_score_prefill_ragged", "topk16_select", "mxfp8_e4m3_quantize"):
         assert name in fns
 
 
