@@ -131,7 +131,8 @@ int topk16_select(const float *scores, int64_t row_stride, int32_t num_rows, int
         return PAGESCORE_EINVAL;
     return launch_status(pagescore::launch_topk16(scores, row_stride, num_rows, width, valid_len,
                                                    force_begin, force_end, append_page, out,
-                                                   out_stride, (hipStream_t)stream));
+                                                   out_stride, current_device_cus(),
+                                                   (hipStream_t)stream));
 }
 
 int mxfp8_e4m3_quantize(const uint16_t *x, int64_t x_stride, int32_t rows, int32_t cols, uint8_t *q,

@@ -45,7 +45,7 @@ hipError_t launch_score_prefill_ragged(const uint8_t *q, const float *q_scale, c
 hipError_t launch_topk16(const float *scores, int64_t row_stride, int32_t num_rows, int32_t width,
                          const int32_t *valid_len, const int32_t *force_begin,
                          const int32_t *force_end, const int32_t *append_page, int32_t *out,
-                         int64_t out_stride, hipStream_t stream);
+                         int64_t out_stride, int num_cus, hipStream_t stream);
 
 hipError_t launch_mxfp8_quant(const uint16_t *x, int64_t ldx, int32_t rows, int32_t cols, uint8_t *q,
                               int64_t ldq, uint8_t *scales, int64_t lds, hipStream_t stream);

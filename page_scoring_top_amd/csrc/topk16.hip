@@ -48,6 +48,7 @@ namespace pagescore {
 namespace {
 
 constexpr int kMaxWavesPerRow = 4;
+constexpr int64_t kUnsplitPasses = 64;             // rows this long stay in one wave (see launch)
 constexpr int kWideLane = 16;                      // columns per lane and pass (1,024 per wave)
 constexpr int kNarrowLane = 4;                     // for rows of at most 256 columns
 constexpr int kBlockWaves = 4;                     // one wave per SIMD
@@ -439,17 +440,23 @@ __global__ __launch_bounds__(256) void topk16_kernel(
 hipError_t launch_topk16(const float *scores, int64_t row_stride, int32_t num_rows, int32_t width,
                          const int32_t *valid_len, const int32_t *force_begin,
                          const int32_t *force_end, const int32_t *append_page, int32_t *out,
-                         int64_t out_stride, hipStream_t stream)
+                         int64_t out_stride, int num_cus, hipStream_t stream)
 {
     // Partitions per row: about one pass (1,024 columns) each, 1, 2 or 4;
     // rows share a work-group of 4 waves.  Rows of at most 256 columns take
-    // 4 columns per lane.
+    // 4 columns per lane.  Rows of 64 passes or more, enough of them to give
+    // every SIMD two waves unsplit, are not split: the partitions' merge and
+    // extra waves then cost more than they spread (2,048 x 65,536: 109 ->
+    // 101 us; 2,048 x 131,072: 200 -> 184 us).
     const bool narrow = width <= kNarrowLane * kWave;
     const int64_t pass_cols = (int64_t)kWideLane * kWave;
     const int64_t passes = ((int64_t)width + pass_cols - 1) / pass_cols;
+    const int64_t simds = (int64_t)(num_cus > 0 ? num_cus : 256) * 4;
     int wpr = 1;
-    while (wpr < kMaxWavesPerRow && wpr < passes)
-        wpr *= 2;
+    if (!(passes >= kUnsplitPasses && num_rows >= 2 * simds)) {
+        while (wpr < kMaxWavesPerRow && wpr < passes)
+            wpr *= 2;
+    }
     const int rows_per_block = kBlockWaves / wpr;
     const int64_t blocks = ((int64_t)num_rows + rows_per_block - 1) / rows_per_block;
     if (blocks > 0x7FFFFFFF)

@@ -84,6 +84,27 @@ def test_prefill_width_rows():
     assert np.array_equal(got[rows], want)
 
 
+def test_long_unsplit_rows():
+    """2,048 rows x 65,536 columns: enough rows of at least 64 passes that each
+    row stays in one wave.  Special rows among them: all-equal scores, NaN every
+    third column, a forced range, a short valid length."""
+    rng = np.random.default_rng(10)
+    W = 65536
+    s = rng.standard_normal((2048, W)).astype(np.float32)
+    s[3] = 2.5
+    s[4, ::3] = np.nan
+    valid = np.full(2048, W, np.int32)
+    valid[7] = 1000
+    fb = np.zeros(2048, np.int32)
+    fe = np.zeros(2048, np.int32)
+    fb[9], fe[9] = 40000, 40005
+    announce("topk 2048 x 65536 unsplit rows")
+    got = gpu_topk(s, W, valid=valid, fb=fb, fe=fe)
+    rows = np.r_[0:12, 2040:2048, rng.choice(2048, 12, replace=False)]
+    want = oracle.topk16(s[rows], valid[rows], fb[rows], fe[rows])
+    assert np.array_equal(got[rows], want)
+
+
 def test_strides_and_rows_past_num_rows():
     rng = np.random.default_rng(3)
     buf = rng.standard_normal((40, 300)).astype(np.float32)
