@@ -105,6 +105,7 @@ int indexer_score_prefill_ragged(const uint8_t *q, const float *q_scale, const u
                                  const int32_t *k_len, int32_t max_q, int32_t width, float *scores,
                                  int64_t ld, int32_t *row_len, void *stream)
 {
+    static_assert(PAGESCORE_RAGGED_MAX_HEADS == pagescore::kRaggedMaxHeads, "header and kernel agree");
     if (T < 0 || N < 0 || H < 1 || H > PAGESCORE_RAGGED_MAX_HEADS || num_seqs < 0 ||
         num_seqs > PAGESCORE_RAGGED_MAX_SEQS || max_q < 0 || width < 1)
         return PAGESCORE_EINVAL;

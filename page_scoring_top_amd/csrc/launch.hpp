@@ -14,6 +14,8 @@ constexpr int32_t kDequantMaxReqs = 65535;
 // Heads per indexer_score_prefill call: a work-group keeps one token's query
 // rows (heads rounded up to 32) as f16 in LDS.
 constexpr int32_t kPrefillMaxHeads = 224;
+// Heads per indexer_score_prefill_ragged call (PAGESCORE_RAGGED_MAX_HEADS).
+constexpr int32_t kRaggedMaxHeads = 64;
 
 // Columns per topk16_select row: a wave reads its share of a row through a
 // buffer descriptor whose byte size and offsets are 32-bit.

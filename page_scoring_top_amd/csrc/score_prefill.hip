@@ -576,6 +576,7 @@ hipError_t launch_score_prefill_ragged(const uint8_t *q, const float *q_scale, c
                                        int32_t width, float *scores, int64_t ld, int32_t *row_len,
                                        hipStream_t stream)
 {
+    static_assert(kRaggedMaxHeads == kSmallHeads, "the ragged batch runs the small-head kernel only");
     if (H > kSmallHeads || num_seqs > 65535)
         return hipErrorInvalidValue;
     const RaggedBatch rb{q_start, k_start, k_len, row_len, width};
