@@ -128,3 +128,45 @@ def test_chain_long_context_sampled():
     check_scores(got[:, :N], want, mag, "long-context prefill")
     assert (got[:, N:].view(np.int32) == CANARY_F32.view(np.int32)).all()
     assert np.array_equal(host(ids)[rows], oracle.topk16(got[:, :N]))
+
+
+def test_chain_ragged_causal_batch():
+    """The whole batch in one causal launch: the gathered pages of all
+    requests are one key buffer (request b's keys start at page_offsets[b] x
+    128), each request's queries are the last tokens of its context, and each
+    row keeps the 16 best of its visible keys."""
+    import page_scoring_top_amd as ps
+    d = workloads.nvfp4_prefill_inputs("nvfp4-prefill-ragged", 77, [37, 100, 1, 64],
+                                       [1000, 3000, 129, 64])
+    announce("nvfp4 prefill chain, ragged causal batch")
+    keys_gpu = gather_gpu(d, extra_pages=0)
+    keys_ora = gather_oracle(d, extra_pages=0)
+    assert np.array_equal(host(keys_gpu), keys_ora), "gathered E4M3 keys differ"
+    T = int(d.tokens.sum())
+    q_start = np.concatenate([[0], np.cumsum(d.tokens)]).astype(np.int32)
+    k_start = (d.page_offsets * 128).astype(np.int32)
+    N = d.total_pages * 128
+    width = int(d.context.max()) + 3
+    ones = np.ones(N, dtype=np.float32)
+    scores = torch.full((T, width + 2), float(CANARY_F32), dtype=torch.float32, device="cuda")
+    row_len = torch.empty(T, dtype=torch.int32, device="cuda")
+    ps.indexer_score_prefill_ragged(dev(d.q), dev(d.q_scale), keys_gpu.view(-1, 128), dev(ones),
+                                    dev(q_start), dev(k_start), dev(d.context),
+                                    int(d.tokens.max()), width, scores, row_len)
+    ids = torch.full((T, 16), int(CANARY_I32), dtype=torch.int32, device="cuda")
+    ps.topk16_select(scores, width, ids, valid_len=row_len)
+    got, got_len, got_ids = host(scores), host(row_len), host(ids)
+    want, want_len = oracle.score_prefill_ragged(d.q, d.q_scale, keys_ora.reshape(-1, 128), ones,
+                                                 q_start, k_start, d.context, width)
+    assert np.array_equal(got_len, want_len), "row lengths differ"
+    assert np.array_equal(np.isneginf(got[:, :width]), np.isneginf(want)), "causal mask differs"
+    assert (got[:, width:].view(np.int32) == CANARY_F32.view(np.int32)).all(), "write past width"
+    for s in range(len(d.tokens)):
+        rows = slice(q_start[s], q_start[s + 1])
+        kl = int(d.context[s])
+        k_ora = keys_ora.reshape(-1, 128)[k_start[s]:k_start[s] + kl]
+        mag = prefill_term_magnitude(d.q[rows], d.q_scale[rows], k_ora, ones[:kl])
+        g, w = got[rows, :kl], want[rows, :kl]
+        vis = ~np.isneginf(w)
+        check_scores(g[vis], w[vis], mag[vis], f"request {s}")
+    assert np.array_equal(got_ids, oracle.topk16(got[:, :width], valid_len=want_len))
