@@ -71,6 +71,22 @@ def test_gather_mtp_config_every_page():
     assert np.array_equal(got, want)
 
 
+def test_gather_long_config_every_page():
+    """The 500K-token batch in the benchmark's launch configuration: every
+    scored page of the 4 requests (15,624 pages, 256 MB of E4M3 out) against
+    the oracle's gather."""
+    d = workloads.long_decode()
+    R, W = d.num_reqs, d.width
+    npages = np.array([min(max((int(s) - 1) // 128, 0), W) for s in d.seq_lens[:R]], np.int32)
+    offs = np.concatenate([[0], np.cumsum(npages)[:-1]]).astype(np.int32)
+    total = int(npages.sum())
+    announce("dequant long config, 15,624 pages")
+    got = _gather(d.kv_cache, d.block_table[:R], npages, offs, W, total)
+    want = np.empty((total, 128, 128), np.uint8)
+    oracle.gather(d.kv_cache, d.block_table[:R], npages, offs, W, want)
+    assert np.array_equal(got, want)
+
+
 def test_nothing_to_do_is_a_no_op():
     import page_scoring_top_amd as ps
     kv = dev(np.zeros((1, 9216), np.uint8))
