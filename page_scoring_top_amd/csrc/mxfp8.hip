@@ -28,6 +28,8 @@ namespace pagescore {
 namespace {
 
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMxWaves = 4;                        // rows per work-group
 constexpr int kMxSteps = 4;                        // 64-lane steps per wave
@@ -52,17 +54,20 @@ __global__ __launch_bounds__(kMxWaves * kWave) void mxfp8_quant_kernel(
         // Unit u holds elements [8u, 8u + 8) of row r; units past the row
         // (whole quads, as a row has a multiple of 4 units) load zeros and
         // store nothing.
-        uint4 v[kMxSteps];
+        // Inputs are read once and codes written once: both streamed past the
+        // caches (nontemporal), 20.0 -> 17.7-18.1 us at 16,384 x 2,048.
+        u32x4 v[kMxSteps];
 #pragma unroll
         for (int j = 0; j < kMxSteps; ++j) {
             const int u = u0 + j * kWave;
-            v[j] = u < units_per_row ? *reinterpret_cast<const uint4 *>(x + r * ldx + 8 * u)
-                                     : make_uint4(0u, 0u, 0u, 0u);
+            v[j] = u < units_per_row
+                       ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + r * ldx + 8 * u))
+                       : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int j = 0; j < kMxSteps; ++j) {
             const int u = u0 + j * kWave;
-            const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+            const uint32_t w[4] = {v[j][0], v[j][1], v[j][2], v[j][3]};
             u16x2 m = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu);
 #pragma unroll
             for (int i = 1; i < 4; ++i)
@@ -90,7 +95,8 @@ __global__ __launch_bounds__(kMxWaves * kWave) void mxfp8_quant_kernel(
                 }
             }
             if (u < units_per_row) {
-                *reinterpret_cast<uint2 *>(q + r * ldq + 8 * u) = make_uint2(out[0], out[1]);
+                __builtin_nontemporal_store(u32x2{out[0], out[1]},
+                                            reinterpret_cast<u32x2 *>(q + r * ldq + 8 * u));
                 if ((lane & 3) == 0)
                     scales[r * lds + u / 4] = (uint8_t)sb;
             }
