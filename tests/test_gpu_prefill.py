@@ -68,7 +68,7 @@ def test_big_config_sampled_rows():
     p = workloads.big_prefill()
     announce("prefill 2048 x 64 x 16384")
     got = gpu_prefill(p)
-    rows = [0, 7, 8, 1029, 2047]
+    rows = [0, 1, 7, 8, 9, 255, 256, 511, 1024, 1029, 1535, 1536, 2039, 2040, 2046, 2047]
     want = oracle.score_prefill_rows(p.q, p.q_scale, p.k, p.k_scale, rows)
     assert_scores_close(got[rows], want, "big prefill")
     assert np.isfinite(got).all()
