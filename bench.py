@@ -42,17 +42,21 @@ METRIC = "index-K GB/s scored (frac of HBM peak) + top-16 rows/s, 500K-token dec
 HBM_PEAK_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "score_decode_long_counters.txt")
 SCORE_SOURCES = ["csrc/score_decode.hip", "csrc/device_common.hpp", "csrc/nvfp4_lut.hpp"]
+MX_COUNTERS_FILE = os.path.join(ROOT, "profiles", "mxfp8_quant_counters.txt")
+MX_SOURCES = ["csrc/mxfp8.hip", "csrc/device_common.hpp", "csrc/nvfp4_lut.hpp"]
+DQ_COUNTERS_FILE = os.path.join(ROOT, "profiles", "nvfp4_dequant_counters.txt")
+DQ_SOURCES = ["csrc/dequant.hip", "csrc/device_common.hpp", "csrc/nvfp4_lut.hpp"]
 
 
-def _score_compile_flags():
-    """hipcc flags of csrc/score_decode.hip from page_scoring_top_amd/build.py
-    (loaded by path), without the machine-specific include paths."""
+def _compile_flags(source):
+    """hipcc flags of csrc/<source> from page_scoring_top_amd/build.py (loaded
+    by path), without the machine-specific include paths."""
     import importlib.util
     spec = importlib.util.spec_from_file_location(
         "_pagescore_build", os.path.join(ROOT, "page_scoring_top_amd", "build.py"))
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
-    flags = mod.common_flags() + mod.FILE_FLAGS.get("score_decode.hip", [])
+    flags = mod.common_flags() + mod.FILE_FLAGS.get(source, [])
     out, skip = [], False
     for f in flags:
         if skip:
@@ -64,27 +68,27 @@ def _score_compile_flags():
     return out
 
 
-def kernel_source_hash() -> str:
-    """Hash of the decode score kernel's sources and compile flags."""
+def kernel_source_hash(sources=SCORE_SOURCES, flags_of="score_decode.hip") -> str:
+    """Hash of a kernel's sources and compile flags (default: the decode scorer)."""
     h = hashlib.sha256()
-    for f in SCORE_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "page_scoring_top_amd", f), "rb") as fh:
             h.update(fh.read())
-    h.update(" ".join(_score_compile_flags()).encode())
+    h.update(" ".join(_compile_flags(flags_of)).encode())
     return h.hexdigest()[:16]
 
 
-def read_counters():
-    """HBM traffic per launch of the score kernel from the committed rocprofv3
-    counter summary, or None when it is missing or the kernel changed since."""
-    if not os.path.exists(COUNTERS_FILE):
+def read_counters(path=COUNTERS_FILE, sources=SCORE_SOURCES, flags_of="score_decode.hip"):
+    """HBM traffic per launch of a kernel from its committed rocprofv3 counter
+    summary, or None when it is missing or the kernel changed since."""
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(COUNTERS_FILE):
+    for line in open(path):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_hash") != kernel_source_hash():
+    if kv.get("source_hash") != kernel_source_hash(sources, flags_of):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -411,6 +415,17 @@ def bench_mxfp8(args):
         q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
         sc = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
         calls.append(ps.prepare(ps.mxfp8_e4m3_quantize, x, q, sc))
+    if args.profile_pass:
+        # Fixed sequence for counter runs: a plain 1 GiB device copy (the
+        # calibration of FETCH_SIZE / WRITE_SIZE), then one launch per set.
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_pass": True, "copy_bytes": 1 << 30, "launches": P}), flush=True)
+        return
     for i in range(args.warmup):
         calls[i % P]()
     torch.cuda.synchronize()
@@ -463,7 +478,8 @@ def bench_mxfp8(args):
                        "mxfp8_e4m3_quantize_128x2048_graph": round(decode_us, 3)},
         "roofline": {"bound": "hbm", "kernel": "mxfp8_e4m3_quantize",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": read_counters(MX_COUNTERS_FILE, MX_SOURCES, "mxfp8.hip"),
                      "algorithmic_bytes_per_launch": algo},
     }
     if not args.no_cpu:
@@ -510,6 +526,16 @@ def bench_dequant(args):
     total = sum(npages)
     out = torch.empty((total, 128, 128), dtype=torch.uint8, device=dev)
     calls = [ps.prepare(ps.nvfp4_index_k_dequant, kv, bt, num_pages, offs, W, out) for kv in pools]
+    if args.profile_pass:
+        # Counter runs: the 1 GiB calibration copy, then one launch per pool.
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_pass": True, "copy_bytes": 1 << 30, "launches": P}), flush=True)
+        return
     stream = torch.cuda.current_stream(dev)
     for i in range(args.warmup):
         calls[i % P]()
@@ -529,7 +555,8 @@ def bench_dequant(args):
         "kernels_us": {"nvfp4_index_k_dequant": round(ms * 1e3, 3)},
         "roofline": {"bound": "hbm", "kernel": "nvfp4_index_k_dequant",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": read_counters(DQ_COUNTERS_FILE, DQ_SOURCES, "dequant.hip"),
                      "algorithmic_bytes_per_launch": algo},
     }
     if not args.no_cpu:
