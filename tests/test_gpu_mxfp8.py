@@ -89,3 +89,12 @@ def test_big_batch_full():
     x = workloads.mx_activations(77, 16384, 2048)
     announce("mxfp8 16384 x 2048")
     check(x, "16384x2048")
+
+
+def test_rows_past_one_grid_column():
+    """262,147 rows: more than 65,535 groups of 4 rows, so work-groups loop
+    over rows (grid y is capped); every byte against the oracle, with a
+    ragged last group."""
+    x = workloads.mx_activations(78, 65535 * 4 + 7, 64)
+    announce("mxfp8 262147 x 64")
+    check(x, "262147x64", x_pad=8, q_pad=16, s_pad=1)
