@@ -55,6 +55,7 @@ constexpr int kMaxWavesPerRow = 4;
 constexpr int kStreamLoad = 2;
 constexpr int64_t kStreamPasses = 8;
 constexpr int64_t kUnsplitPasses = 64;             // rows this long stay in one wave (see launch)
+constexpr int64_t kHalfSplitPasses = 8;            // rows of 8..31 passes take two partitions (see launch)
 constexpr int kWideLane = 16;                      // columns per lane and pass (1,024 per wave)
 constexpr int kNarrowLane = 4;                     // for rows of at most 256 columns
 constexpr int kBlockWaves = 4;                     // one wave per SIMD
@@ -453,14 +454,17 @@ hipError_t launch_topk16(const float *scores, int64_t row_stride, int32_t num_ro
     // 4 columns per lane.  Rows of 64 passes or more, enough of them to give
     // every SIMD two waves unsplit, are not split: the partitions' merge and
     // extra waves then cost more than they spread (2,048 x 65,536: 109 ->
-    // 101 us; 2,048 x 131,072: 200 -> 184 us).
+    // 101 us; 2,048 x 131,072: 200 -> 184 us).  Rows of 8 to 31 passes take
+    // two partitions (2,048 x 16,384: 31.1 -> 29.6 us; 8,192 to 24,576
+    // columns gain 3-5%), while 32 passes measured 4% slower with two.
     const bool narrow = width <= kNarrowLane * kWave;
     const int64_t pass_cols = (int64_t)kWideLane * kWave;
     const int64_t passes = ((int64_t)width + pass_cols - 1) / pass_cols;
     const int64_t simds = (int64_t)(num_cus > 0 ? num_cus : 256) * 4;
     int wpr = 1;
     if (!(passes >= kUnsplitPasses && num_rows >= 2 * simds)) {
-        while (wpr < kMaxWavesPerRow && wpr < passes)
+        const int cap = (passes >= kHalfSplitPasses && passes < 4 * kHalfSplitPasses) ? 2 : kMaxWavesPerRow;
+        while (wpr < cap && wpr < passes)
             wpr *= 2;
     }
     const int rows_per_block = kBlockWaves / wpr;

@@ -23,7 +23,8 @@ def gpu_topk(scores, width, valid=None, fb=None, fe=None, ap=None, num_rows=None
     return host(out)
 
 
-WIDTHS = [1, 2, 15, 16, 17, 63, 64, 65, 100, 255, 768, 769, 1344, 3907, 5000]
+WIDTHS = [1, 2, 15, 16, 17, 63, 64, 65, 100, 255, 768, 769, 1344, 3907, 5000,
+          8191, 8193, 32768, 40000]   # two partitions at 8-31 passes, four at 32-63
 
 
 @pytest.mark.parametrize("width", WIDTHS)
