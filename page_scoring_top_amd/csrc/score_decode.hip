@@ -204,7 +204,8 @@ __device__ __forceinline__ void finish_request(RequestRegs &rq, const RequestRaw
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             dst[k] = q_word_f16(r.bytes[hf][2 * k], r.bytes[hf][2 * k + 1]);
-            nan |= has_nan_byte(r.bytes[hf][2 * k]) | has_nan_byte(r.bytes[hf][2 * k + 1]);
+            nan |= has_nan_byte(r.bytes[hf][2 * k]);
+            nan |= has_nan_byte(r.bytes[hf][2 * k + 1]);
         }
         // A row is NaN when any of its four depth chunks (lanes m, m+16, m+32, m+48) is.
         int f = nan ? 1 : 0;
@@ -404,8 +405,10 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
         // Lanes without a row have own = -1 and store nothing.
         if (cur_ok && j < rq.own) {
             float s = (v + fabsf(v)) * 0.5f * rq.qs;
+            // The file is built without NaN semantics, so the NaN is written
+            // as its bit pattern (the canonical quiet NaN).
             if (page_nan || rq.qnan)
-                s = __builtin_nanf("");
+                s = __uint_as_float(0x7FC00000u);
             scores[((int64_t)b * kDecodeRows + store_row(lane)) * width + j] = s;
         }
         cur_ok = nxt_ok;

@@ -96,13 +96,6 @@ __device__ __forceinline__ int lanes_set(uint64_t mask)
     return __builtin_popcount((uint32_t)mask) + __builtin_popcount((uint32_t)(mask >> 32));
 }
 
-// Set bits of `mask` below this lane.
-__device__ __forceinline__ int bits_below(uint64_t mask)
-{
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
 // Orders this wave's LDS accesses before and after (a wave's LDS operations
 // execute in order; this stops the compiler from moving them across).
 __device__ __forceinline__ void wave_lds_sync()
