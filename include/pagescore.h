@@ -66,12 +66,15 @@ extern "C" {
  *   kv_cache          [num_blocks pages] at page_stride_bytes apart; 16-byte
  *                     aligned, page_stride_bytes >= 9216 and a multiple of 16.
  *   num_blocks        pages in kv_cache (>= 1 when anything is gathered).
- *   block_table       [num_reqs, bt_stride] int32 physical page ids.
- *   num_pages         [num_reqs] int32 logical pages to gather per request.
- *   page_offsets      [num_reqs] int32 first output page of each request.
- *   max_num_pages     host upper bound of num_pages; request r gathers its
- *                     first min(num_pages[r], max_num_pages) pages, so
- *                     bt_stride must be >= max_num_pages.
+ *   block_table       [num_reqs, bt_stride] int32: entry (r, j) is the index
+ *                     in kv_cache of the page holding request r's logical
+ *                     page j.
+ *   num_pages         [num_reqs] int32: how many logical pages request r has.
+ *   page_offsets      [num_reqs] int32: the page of out that receives request
+ *                     r's logical page 0 (its later pages follow it).
+ *   max_num_pages     a cap, known on the host, on the pages of one request:
+ *                     request r gathers min(num_pages[r], max_num_pages)
+ *                     pages, so bt_stride must be >= max_num_pages.
  *   out               [out_pages, 128, 128] E4M3 bytes, 16-byte aligned;
  *                     output page page_offsets[r] + j gets logical page j of
  *                     request r.  Nothing else is written.
@@ -121,6 +124,8 @@ int nvfp4_index_k_dequant(const uint8_t *kv_cache, int64_t page_stride_bytes,
  *                     its contents.
  *   row_own           nullable [num_reqs, 32] int32; receives every row's own
  *                     page, or -1 for rows without a query.
+ * A page whose block-table id lies outside [0, num_blocks) is not read, and
+ * its column of every row keeps its contents.
  * num_reqs == 0 returns PAGESCORE_OK with no launch; at most 65535 requests
  * per call (one grid row per request).
  */

@@ -1,8 +1,10 @@
 """GPU parity of indexer_score_decode against the oracle.
 
-Scores within |gpu - oracle| <= 1e-6 + 1e-5 |oracle| (NaN meets NaN), own
-pages exact, and every entry the call must not write (columns at or past a
-row's own page, rows without a query, padding requests) bit-unchanged.
+Every stored score within |gpu - oracle| <= 1e-6 + 1e-5 |oracle| (NaN meets
+NaN), own pages exact, and every entry the call must not write (columns at
+or past a row's own page, rows without a query, padding requests, pages
+whose id is out of range) bit-unchanged.  The large configurations are
+compared in full too: the oracle runs on host threads (tests/oracle_pool.py).
 """
 
 import numpy as np
@@ -10,6 +12,7 @@ import pytest
 import torch
 
 import oracle
+import oracle_pool
 import workloads
 from gpu_util import CANARY_F32, CANARY_I32, announce, assert_scores_close, dev, host
 
@@ -50,32 +53,27 @@ def written_mask(d, own):
     return m
 
 
-def check_full(d, got_scores, got_own):
+def check_full(d, got_scores, got_own, pooled=False):
+    """Every entry of the score buffer: stored ones against the oracle, the
+    rest bit-unchanged.  ``pooled`` runs the oracle on host threads."""
     want_own = expected_own(d)
     assert np.array_equal(got_own, want_own), "row_own differs"
-    want = np.full(got_scores.shape, CANARY_F32, np.float32)
-    want[:d.num_reqs], _ = oracle.score_decode(d.kv_cache, d.block_table, d.seq_lens, d.q,
-                                               d.q_scale, d.num_reqs, d.qlen, d.width,
-                                               scores=want[:d.num_reqs].copy())
+    base = np.full(got_scores.shape, CANARY_F32, np.float32)
+    if pooled:
+        want, stored = oracle_pool.score_decode(d, base=base)
+    else:
+        want = base
+        want[:d.num_reqs], _ = oracle.score_decode(d.kv_cache, d.block_table, d.seq_lens, d.q,
+                                                   d.q_scale, d.num_reqs, d.qlen, d.width,
+                                                   scores=want[:d.num_reqs].copy())
+        stored = None
     m = written_mask(d, want_own)
+    if stored is not None:
+        assert np.array_equal(stored, m), "the oracle's stored region differs from the geometry"
     assert np.array_equal(got_scores[~m].view(np.int32), want[~m].view(np.int32)), \
         "an entry outside the stored region was written"
     assert_scores_close(got_scores[m], want[m], d.name)
-
-
-def check_sampled(d, got_scores, got_own, columns):
-    want_own = expected_own(d)
-    assert np.array_equal(got_own, want_own), "row_own differs"
-    m = written_mask(d, want_own)
-    assert (got_scores[~m].view(np.int32) == CANARY_F32.view(np.int32)).all(), \
-        "an entry outside the stored region was written"
-    assert not (got_scores[m].view(np.int32) == CANARY_F32.view(np.int32)).any(), \
-        "an entry of the stored region was not written"
-    for b, j in columns:
-        col, stored = oracle.score_decode_column(d.kv_cache, d.block_table, d.seq_lens, d.q,
-                                                 d.q_scale, d.qlen, d.width, b, j)
-        assert np.array_equal(stored, m[b, :, j])
-        assert_scores_close(got_scores[b, stored, j], col[stored], f"{d.name} b={b} j={j}")
+    return int(m.sum())
 
 
 def test_tiny_config_full():
@@ -124,40 +122,65 @@ def test_all_nan_free_scales_with_negatives():
     check_full(d, s, own)
 
 
-def test_mtp_config():
+def test_mtp_config_full():
+    """16 requests x 8 slots at 30,000 tokens: all 512 rows x 234 pages."""
     d = workloads.mtp_decode()
-    announce("decode mtp (16 req x 8 slots, 30,000 tokens)")
+    announce("decode mtp (16 req x 8 slots, 30,000 tokens), every score")
     s, own = run_decode(d)
-    rng = np.random.default_rng(0)
-    cols = [(0, j) for j in range(0, 234, 9)] + \
-           [(int(rng.integers(0, 16)), int(rng.integers(0, 234))) for _ in range(24)] + \
-           [(15, 233), (7, 0)]
-    check_sampled(d, s, own, cols)
+    assert check_full(d, s, own, pooled=True) == 16 * 32 * 234
 
 
-def test_ragged_config_with_padding_requests():
+def test_ragged_config_full_with_padding_requests():
+    """64 requests with contexts of 1,000..172,032 tokens and 8 padding
+    requests, width 1,344: every stored score of the 2,048 real rows."""
     d = workloads.ragged_decode()
-    announce("decode ragged (64 req + 8 padding, width 1344)")
+    announce("decode ragged (64 req + 8 padding, width 1344), every score")
     s, own = run_decode(d)
-    rng = np.random.default_rng(1)
-    cols = []
-    for b in rng.choice(64, size=12, replace=False):
-        npg = min(oracle.decode_pages(int(d.seq_lens[b])), d.width)
-        cols += [(int(b), 0), (int(b), npg - 1), (int(b), int(rng.integers(0, npg)))]
-    check_sampled(d, s, own, cols)
+    n = check_full(d, s, own, pooled=True)
+    assert n > 0
     assert (s[64:].view(np.int32) == CANARY_F32.view(np.int32)).all()
     assert (own[64:] == CANARY_I32).all()
 
 
-def test_long_config_sampled_and_deterministic():
-    """The 500,000-token configuration in the launch configuration the benchmark
-    times; sampled columns against the oracle, every write region checked, and
-    two runs bit-identical."""
+def test_long_config_full_and_deterministic():
+    """The 500,000-token configuration in the launch configuration the
+    benchmark times: all 128 rows x 3,906 pages against the oracle, and two
+    runs bit-identical."""
     d = workloads.long_decode()
-    announce("decode long (4 req x 8 slots, 500,000 tokens)")
+    announce("decode long (4 req x 8 slots, 500,000 tokens), every score")
     (s1, s2), own = run_decode(d, repeat=2)
     assert np.array_equal(s1.view(np.int32), s2.view(np.int32)), "not deterministic"
-    rng = np.random.default_rng(2)
-    cols = [(b, j) for b in range(4) for j in (0, 1, 1234, 3905)] + \
-           [(int(rng.integers(0, 4)), int(rng.integers(0, 3906))) for _ in range(12)]
-    check_sampled(d, s1, own, cols)
+    assert check_full(d, s1, own, pooled=True) == 4 * 32 * 3906
+
+
+def test_out_of_range_page_ids_are_skipped():
+    """Block-table ids below 0 or at and past num_blocks: such a page is not
+    read and its column keeps its canaries in every row; every other column
+    matches the oracle (which is given a valid id in their place)."""
+    d = workloads.decode_inputs("bad-ids", 11, [3000, 2500, 1800], qlen=8, width=24)
+    nb = d.num_blocks
+    bad = {(0, 0): -1, (0, 5): nb, (0, 22): -2147483648, (1, 3): nb + 1000,
+           (1, 18): 2147483647, (2, 7): -7, (2, 13): nb}
+    bt_gpu = d.block_table.copy()
+    for (b, j), v in bad.items():
+        bt_gpu[b, j] = v
+    announce("decode out-of-range page ids")
+    import page_scoring_top_amd as ps
+    scores = torch.full((3, 32, d.width), float(CANARY_F32), dtype=torch.float32, device="cuda")
+    own = torch.full((3, 32), int(CANARY_I32), dtype=torch.int32, device="cuda")
+    ps.indexer_score_decode(dev(d.kv_cache), dev(bt_gpu), dev(d.seq_lens), dev(d.q),
+                            dev(d.q_scale), d.qlen, d.width, scores, own, num_reqs=3)
+    got, got_own = host(scores), host(own)
+    want_own = expected_own(d)
+    assert np.array_equal(got_own, want_own)
+    want, _ = oracle.score_decode(d.kv_cache, d.block_table, d.seq_lens, d.q, d.q_scale, 3,
+                                  d.qlen, d.width,
+                                  scores=np.full(got.shape, CANARY_F32, np.float32))
+    m = written_mask(d, want_own)
+    for (b, j) in bad:
+        assert m[b, :, j].any(), "the test must put a bad id in a scored column"
+        m[b, :, j] = False
+    assert np.array_equal(got[~m].view(np.int32),
+                          np.full(got.shape, CANARY_F32, np.float32)[~m].view(np.int32)), \
+        "a column with an out-of-range id, or outside the stored region, was written"
+    assert_scores_close(got[m], want[m], "bad ids")

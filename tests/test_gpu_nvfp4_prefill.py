@@ -13,16 +13,18 @@ GPU's own score rows.
 Score tolerance.  Block scales span the whole positive E4M3 range, so keys
 reach 448 and a token's dot products can cancel to a result far below their
 terms; an f32 accumulation is then off by a few units in the last place of
-the terms, not of the result.  Scores are compared with
-|gpu - oracle| <= 1e-6 + 1e-5 max(|oracle|, M), M = k_scale * sum_h q_scale *
-sum_d |q k| (the size of the summed terms), and at most 0.1% of them may need
-M, i.e. fall outside 1e-6 + 1e-5 |oracle|."""
+the terms, not of the result.  This path therefore does not meet the plain
+bound |gpu - oracle| <= 1e-6 + 1e-5 |oracle| on every score.  Every score
+must meet |gpu - oracle| <= 1e-6 + 1e-5 max(|oracle|, M), M = k_scale *
+sum_h q_scale * sum_d |q k| (the size of the summed terms); the scores
+outside the plain bound are counted, printed, and may be at most 0.1%."""
 
 import numpy as np
 import pytest
 import torch
 
 import oracle
+import oracle_pool
 import workloads
 from gpu_util import (ATOL, CANARY_F32, CANARY_I32, RTOL, announce, assert_scores_close, dev, host,
                       prefill_term_magnitude)
@@ -52,10 +54,15 @@ def request_keys(keys, d, b):
 
 
 def check_scores(got, want, magnitude, what):
+    """Every score within the term bound; returns (outside the plain bound,
+    compared), which is printed and may be at most 0.1%."""
     assert_scores_close(got, want, what, magnitude=magnitude)
     fin = np.isfinite(want)
     plain = np.abs(got[fin].astype(np.float64) - want[fin]) <= ATOL + RTOL * np.abs(want[fin])
-    assert (~plain).sum() <= 1e-3 * fin.sum(), f"{what}: {(~plain).sum()} scores need the term bound"
+    n_out, n = int((~plain).sum()), int(fin.sum())
+    print(f"[nvfp4-prefill] {what}: {n_out} of {n} scores outside the plain bound", flush=True)
+    assert n_out <= 1e-3 * n, f"{what}: {n_out} scores need the term bound"
+    return n_out, n
 
 
 def run_chain(d: workloads.Nvfp4PrefillInputs, keys_gpu):
@@ -107,27 +114,33 @@ def test_chain_small(tokens, contexts, heads):
         t0 += T
 
 
-def test_chain_long_context_sampled():
+@pytest.mark.timeout(600)
+def test_chain_long_context_rows_of_every_wave():
     """A 2,048-token chunk with 4 heads against a 65,536-token context (512
-    pages), in the benchmark's launch configuration: every gathered byte,
-    full score rows of tokens at the edges of waves and work-groups, and the
-    top-16 of those rows."""
+    pages), in the benchmark's launch configuration (16 tokens per wave,
+    eight waves per work-group, 16 token groups): every gathered byte; two
+    full score rows from every (token group, wave), their positions in the
+    wave cycling through all 16; and the top-16 of all 2,048 rows against
+    the oracle's selection over the GPU's own scores."""
     d = workloads.nvfp4_prefill()
     announce("nvfp4 prefill 2048 x 4 heads x 65536 keys")
     keys_gpu = gather_gpu(d, extra_pages=0)
     keys_ora = gather_oracle(d, extra_pages=0)
     assert np.array_equal(host(keys_gpu), keys_ora), "gathered E4M3 keys differ"
     (scores, ids), = run_chain(d, keys_gpu)
-    rows = [0, 1, 7, 8, 63, 64, 1029, 2040, 2047]
-    got = host(scores[rows])
     N = int(d.context[0])
+    got_all = host(scores)
+    assert (got_all[:, N:].view(np.int32) == CANARY_F32.view(np.int32)).all()
+    rows = sorted({128 * g + 16 * w + (8 * g + w + 8 * r) % 16
+                   for g in range(16) for w in range(8) for r in range(2)})
+    assert len(rows) == 256
+    got = got_all[rows]
     k_ora = request_keys(keys_ora, d, 0)
     ones = np.ones(N, dtype=np.float32)
-    want = oracle.score_prefill_rows(d.q, d.q_scale, k_ora, ones, rows)
+    want = oracle_pool.score_prefill_rows(d.q, d.q_scale, k_ora, ones, rows)
     mag = prefill_term_magnitude(d.q[rows], d.q_scale[rows], k_ora, ones)
     check_scores(got[:, :N], want, mag, "long-context prefill")
-    assert (got[:, N:].view(np.int32) == CANARY_F32.view(np.int32)).all()
-    assert np.array_equal(host(ids)[rows], oracle.topk16(got[:, :N]))
+    assert np.array_equal(host(ids), oracle_pool.topk16(got_all[:, :N])), "top-16 differ"
 
 
 def test_chain_ragged_causal_batch():

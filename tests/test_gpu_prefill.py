@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle
+import oracle_pool
 import workloads
 from gpu_util import CANARY_F32, announce, assert_scores_close, dev, host
 
@@ -61,14 +62,16 @@ def test_nan_inputs_propagate():
     assert_scores_close(got, want, "nan inputs")
 
 
-def test_big_config_sampled_rows():
+@pytest.mark.timeout(600)
+def test_big_config_rows_of_every_group():
     """2,048 tokens x 64 heads x 16,384 keys in the benchmark's launch
-    configuration; full rows of first, middle and last tokens of work-groups
-    against the oracle."""
+    configuration (one token per wave, eight waves per work-group, 256
+    work-groups over all keys): one full row from every work-group, the
+    wave position cycling through all eight, against the oracle."""
     p = workloads.big_prefill()
     announce("prefill 2048 x 64 x 16384")
     got = gpu_prefill(p)
-    rows = [0, 1, 7, 8, 9, 255, 256, 511, 1024, 1029, 1535, 1536, 2039, 2040, 2046, 2047]
-    want = oracle.score_prefill_rows(p.q, p.q_scale, p.k, p.k_scale, rows)
-    assert_scores_close(got[rows], want, "big prefill")
     assert np.isfinite(got).all()
+    rows = [8 * g + (g % 8) for g in range(256)]
+    want = oracle_pool.score_prefill_rows(p.q, p.q_scale, p.k, p.k_scale, rows)
+    assert_scores_close(got[rows], want, "big prefill")

@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+import oracle_pool
 import workloads
 from gpu_util import CANARY_F32, CANARY_I32, announce, assert_scores_close, dev, host
 
@@ -84,22 +85,35 @@ def test_width_below_context():
     assert (got[:, width:].view(np.int32) == CANARY_F32.view(np.int32)).all()
 
 
-def test_big_batch_sampled_rows():
+@pytest.mark.timeout(600)
+def test_big_batch_rows_of_every_wave():
     """Four sequences of 512 queries with 4,096 .. 16,384-token contexts and
     64 heads (2,048 rows x 16,384 columns, the benchmark's launch
-    configuration): sampled full rows against the oracle."""
+    configuration): 33 full rows of every sequence -- one per two work-groups
+    of eight queries, the wave position cycling through all eight, and the
+    last query -- against the oracle; the -inf fill of all 2,048 rows."""
     d = workloads.ragged_prefill()
     announce("ragged prefill 4 x 512 x 64 heads, contexts 4096..16384")
     got, row_len, _ = run(d.p, d.q_start, d.k_start, d.k_len, d.width, d.width)
-    rows = [0, 1, 511, 512, 1000, 1535, 1536, 2047]
-    for t in rows:
-        s = int(np.searchsorted(d.q_start, t, side="right") - 1)
-        i = t - int(d.q_start[s])
+    pieces = []
+    for s in range(len(d.k_len)):
         q_len = int(d.q_start[s + 1] - d.q_start[s])
-        c = oracle.causal_count(q_len, int(d.k_len[s]), i, d.width)
-        assert row_len[t] == c
+        for i in [16 * k + (k % 8) for k in range(32)] + [q_len - 1]:
+            pieces.append((s, int(d.q_start[s]) + i, oracle.causal_count(q_len, int(d.k_len[s]), i,
+                                                                         d.width)))
+    for s in range(len(d.k_len)):
+        q_len = int(d.q_start[s + 1] - d.q_start[s])
+        for i in range(q_len):
+            t = int(d.q_start[s]) + i
+            c = oracle.causal_count(q_len, int(d.k_len[s]), i, d.width)
+            assert row_len[t] == c, f"row_len of row {t}"
+            assert np.all(np.isneginf(got[t, c:])), f"-inf fill of row {t}"
+
+    def one(piece):
+        s, t, c = piece
         k0 = int(d.k_start[s])
-        want = oracle.score_prefill_rows(d.p.q, d.p.q_scale, d.p.k[k0:k0 + c], d.p.k_scale[k0:k0 + c],
-                                         [t])[0]
+        return oracle.score_prefill_rows(d.p.q, d.p.q_scale, d.p.k[k0:k0 + c],
+                                         d.p.k_scale[k0:k0 + c], [t])[0]
+
+    for (s, t, c), want in zip(pieces, oracle_pool.map_pieces(one, pieces, "ragged rows")):
         assert_scores_close(got[t, :c], want, f"row {t}")
-        assert np.all(np.isneginf(got[t, c:]))

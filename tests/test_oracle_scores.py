@@ -181,3 +181,43 @@ def test_decode_writes_only_below_own_page():
             limit = min(max(o, 0), 4, oracle.decode_pages(seq))
             assert (scores[b, row, :limit] != canary).all()
             assert (scores[b, row, limit:] == canary).all()
+
+
+def test_prefill_rows_equal_the_full_prefill():
+    """score_prefill_rows, the checker of sampled rows, is the full score
+    restricted to the rows asked for: same bits, in the order asked
+    (repeated and unsorted rows included)."""
+    p = workloads.prefill_inputs("rows", 12, 11, 6, 45)
+    full = oracle.score_prefill(p.q, p.q_scale, p.k, p.k_scale)
+    rows = [10, 0, 3, 3, 7, 1, 10]
+    got = oracle.score_prefill_rows(p.q, p.q_scale, p.k, p.k_scale, rows)
+    assert np.array_equal(got.view(np.int32), full[rows].view(np.int32))
+
+
+def test_prefill_rows_exact_rational():
+    """score_prefill_rows against an exact rational evaluation of
+    k_scale * sum_h relu(q_h . k) * q_scale_h on wide-range E4M3 inputs with
+    signed scales; the oracle rounds its double head sum once to float, so
+    it must be the float nearest to the exact value or a neighbour of it
+    (the double sum may sit on the other side of a float midpoint)."""
+    rng = np.random.default_rng(13)
+    T, H, N = 4, 3, 9
+    q = _finite_e4m3_bytes(rng, T * H * 128).reshape(T, H, 128)
+    k = _finite_e4m3_bytes(rng, N * 128).reshape(N, 128)
+    qs = rng.uniform(-2.0, 2.0, size=(T, H)).astype(np.float32)
+    ks = rng.uniform(-2.0, 2.0, size=(N,)).astype(np.float32)
+    rows = [2, 0, 3]
+    got = oracle.score_prefill_rows(q, qs, k, ks, rows)
+    for i, t in enumerate(rows):
+        for n in range(N):
+            acc = Fraction(0)
+            for h in range(H):
+                dot = sum(_e4m3_frac(int(a)) * _e4m3_frac(int(b)) for a, b in zip(q[t, h], k[n]))
+                acc += max(dot, Fraction(0)) * Fraction(float(qs[t, h]))
+            exact = Fraction(float(ks[n])) * acc
+            g = np.float32(got[i, n])
+            lo, hi = np.nextafter(g, np.float32(-np.inf)), np.nextafter(g, np.float32(np.inf))
+            assert Fraction(float(lo)) <= exact <= Fraction(float(hi)), (t, n)
+            # and it is within half a float ulp plus the double rounding
+            assert abs(Fraction(float(g)) - exact) <= (Fraction(float(hi)) - Fraction(float(g))) \
+                * Fraction(1, 2) * (1 + Fraction(1, 2 ** 20)) + abs(exact) * Fraction(1, 2 ** 50)
