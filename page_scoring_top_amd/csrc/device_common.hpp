@@ -66,6 +66,17 @@ __device__ __forceinline__ bool scale_is_nan(uint32_t scale_byte)
     return (scale_byte & 0x7Fu) == 0x7Fu;
 }
 
+// Orders LDS stores of some lanes of a wave before loads of other lanes of
+// the same wave (and the reverse): a wave-scope release/acquire around the
+// wave barrier.  At wavefront scope this emits no instruction; it only keeps
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // A raw buffer descriptor over `bytes` bytes at `base` (wave-uniform by
 // construction).  Loads at or past `bytes` read zeros and stores there are
 // dropped, without touching memory; a descriptor of 0 bytes makes every

@@ -33,12 +33,16 @@
 //
 // Each output lane of a 16x16 tile holds 4 tokens of one query row, so the
 // page maximum is a running per-lane max over the 8 tiles, then 2 cross-lane
-// steps.  With the 16-cycle MFMA a wave hides only about one VALU instruction
-// behind each MFMA (measured), so the per-page cost is close to the sum of
-// both: the dequantization keeps to 12 VALU operations per 8 elements, and
-// the MFMA results stay in VGPRs.  The table is signed (a negative scale's
-// entry carries the sign bit and the code's sign is XOR-ed in), so negative
-// scales need no extra work and every page takes the same path.
+// steps.  A wave cannot issue VALU work while its own MFMAs run, and the
+// VALU of a second wave on the SIMD runs at about half rate meanwhile
+// (measured), so the per-page cost is close to the sum of both: the
+// dequantization keeps to 12 VALU operations per 8 elements, the MFMA
+// results stay in VGPRs, and tiles are taken in pairs -- a burst of
+// dequantization for two tiles, then their 16 MFMAs -- so that the two waves
+// of a SIMD can overlap one's VALU burst with the other's MFMA burst.  The
+// table is signed (a negative scale's entry carries the sign bit and the
+// code's sign is XOR-ed in), so negative scales need no extra work and every
+// page takes the same path.
 //
 // Scheduling: work-group (x, b) covers request b; each of its waves owns a run
 // of `chunk` consecutive pages (chosen on the host from the batch size).  A
@@ -52,9 +56,12 @@
 // nothing).  Runs past a request's last page exit at once, and the hardware
 // dispatcher back-fills the compute units, which balances ragged batches.
 //
-// NaN: the MFMA's NaN handling is not relied on.  A NaN scale byte makes every
-// dot of its token NaN, so it marks the whole page NaN; a NaN byte in a query
-// row marks the row NaN.  Both are tracked as flags and applied at the store.
+// NaN propagates through the arithmetic itself: a NaN scale byte gives its
+// group NaN keys (the table entry of a NaN scale is all 0x7F), a NaN query
+// byte a NaN query element, the f16 MFMA carries a NaN operand into every dot
+// it enters, and the page maximum is taken with v_maximum3_f32, which
+// propagates NaN (IEEE 754-2019 maximum).  So a NaN scale makes its token's
+// dots, and the page score, NaN; a NaN query byte makes its row NaN.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -106,9 +113,11 @@ __device__ __forceinline__ void unpack_scales(const PageRegs &p, uint8_t *stage,
                                               int g, uint32_t sc[8])
 {
     *reinterpret_cast<u32x4 *>(stage + 16 * lane) = p.scales;
+    wave_lds_sync();   // other lanes' bytes are read next
 #pragma unroll
     for (int t = 0; t < 8; ++t)
         sc[t] = *reinterpret_cast<const uint16_t *>(stage + (16 * t + m) * 8 + 2 * g);
+    wave_lds_sync();   // before the next page's block overwrites the area
 }
 
 // E4M3 bytes [0,2,4,6] and [1,3,5,7] of a word -> the four f16 pairs (0,2) (4,6) (1,3) (5,7).
@@ -123,13 +132,6 @@ __device__ __forceinline__ u32x4 f16_word(uint32_t even, uint32_t odd)
 __device__ __forceinline__ u32x4 q_word_f16(uint32_t lo, uint32_t hi)
 {
     return f16_word(byte_perm(hi, lo, 0x06040200u), byte_perm(hi, lo, 0x07050301u));
-}
-
-__device__ __forceinline__ bool has_nan_byte(uint32_t w)
-{
-    // A byte is NaN iff its low 7 bits are all ones.
-    const uint32_t x = w & 0x7F7F7F7Fu;
-    return ((x + 0x01010101u) & 0x80808080u) != 0;
 }
 
 __device__ __forceinline__ int decode_own(int32_t seq, int32_t qlen, int slot)
@@ -158,7 +160,6 @@ struct RequestRegs {
     u32x4 qa[4], qb[4];  // B operands (f16): query rows m and 16+m, chunk g, per code word
     int own;             // own page of row store_row(lane) (-1 for other lanes)
     float qs;            // q_scale of that row
-    bool qnan;           // that row has a NaN query byte
 };
 
 // Raw query bytes (rows m and 16+m, depth chunk g) and the q_scale of row
@@ -196,33 +197,14 @@ __device__ __forceinline__ void load_request_raw(RequestRaw &r, const uint8_t *_
 __device__ __forceinline__ void finish_request(RequestRegs &rq, const RequestRaw &r, int32_t seq,
                                                int32_t qlen, int lane)
 {
-    bool nan_half[2];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-        u32x4 *dst = hf == 0 ? rq.qa : rq.qb;
-        bool nan = false;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            dst[k] = q_word_f16(r.bytes[hf][2 * k], r.bytes[hf][2 * k + 1]);
-            nan |= has_nan_byte(r.bytes[hf][2 * k]);
-            nan |= has_nan_byte(r.bytes[hf][2 * k + 1]);
-        }
-        // A row is NaN when any of its four depth chunks (lanes m, m+16, m+32, m+48) is.
-        int f = nan ? 1 : 0;
-        f |= __shfl_xor(f, 16);
-        f |= __shfl_xor(f, 32);
-        nan_half[hf] = f != 0;
+    for (int k = 0; k < 4; ++k) {
+        rq.qa[k] = q_word_f16(r.bytes[0][2 * k], r.bytes[0][2 * k + 1]);
+        rq.qb[k] = q_word_f16(r.bytes[1][2 * k], r.bytes[1][2 * k + 1]);
     }
     const int row = store_row(lane);
-    if (row >= 0) {
-        rq.own = decode_own(seq, qlen, row / kDecodeHeads);
-        rq.qs = r.qs;
-        rq.qnan = row < 16 ? nan_half[0] : nan_half[1];
-    } else {
-        rq.own = -1;
-        rq.qs = 0.0f;
-        rq.qnan = false;
-    }
+    rq.own = row >= 0 ? decode_own(seq, qlen, row / kDecodeHeads) : -1;
+    rq.qs = row >= 0 ? r.qs : 0.0f;
 }
 
 // Dequantize the 8 E2M1 codes of one word against a signed table entry
@@ -238,6 +220,11 @@ __device__ __forceinline__ void dequant_word_signed(uint32_t codes, uint32_t lut
     odd = mag_o ^ (codes & 0x80808080u);
 }
 
+__device__ __forceinline__ float max3(float a, float b, float c)
+{
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
 // Score one page for the request's 32 rows: rmax is the page maximum of the
 // raw dot products of row store_row(lane).  Each tile's code registers are
 // refilled from nsrc (the next page) once the tile is scored.
@@ -250,62 +237,69 @@ __device__ __forceinline__ void score_page(PageRegs &p, const uint32_t sc[8],
     v4f mx0 = {ninf, ninf, ninf, ninf};
     v4f mx1 = mx0;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int tp = 0; tp < 4; ++tp) {
         // The fence keeps the compiler from hoisting the selector arithmetic
-        // of all eight tiles to the top of the page, which would hold dozens
-        // of registers live at once.
+        // of later tiles to the top of the page, which would hold dozens of
+        // registers live at once.
         __builtin_amdgcn_sched_barrier(0);
-        const uint32_t w[4] = {p.codes[t][0], p.codes[t][1], p.codes[t][2], p.codes[t][3]};
-        v4f c0 = {0.f, 0.f, 0.f, 0.f};
-        v4f c1 = c0;
+        v8h av[2][4];   // A operands (f16 keys) of tiles 2tp and 2tp+1, per code word
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const uint64_t e = lut[(sc[t] >> (8 * hh)) & 0xFFu];
+        for (int u = 0; u < 2; ++u) {
+            const int t = 2 * tp + u;
+            const uint32_t w[4] = {p.codes[t][0], p.codes[t][1], p.codes[t][2], p.codes[t][3]};
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                uint32_t ev, od;
-                dequant_word_signed(w[2 * hh + k], uint32_t(e >> 32), uint32_t(e), ev, od);
-                const v8h av = __builtin_bit_cast(v8h, f16_word(ev, od));
-                c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    av, __builtin_bit_cast(v8h, rq.qa[2 * hh + k]), c0, 0, 0, 0);
-                c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    av, __builtin_bit_cast(v8h, rq.qb[2 * hh + k]), c1, 0, 0, 0);
+            for (int hh = 0; hh < 2; ++hh) {
+                const uint64_t e = lut[(sc[t] >> (8 * hh)) & 0xFFu];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    uint32_t ev, od;
+                    dequant_word_signed(w[2 * hh + k], uint32_t(e >> 32), uint32_t(e), ev, od);
+                    av[u][2 * hh + k] = __builtin_bit_cast(v8h, f16_word(ev, od));
+                }
             }
         }
-        // This tile's code registers are free: they take the next page's.
-        p.codes[t] = __builtin_amdgcn_raw_buffer_load_b128(nsrc, (16 * t + m) * 64 + 16 * g, 0,
-                                                           kStreamLoad);
+        v4f c[2][2];    // [tile][query half]
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            c[u][0] = v4f{0.f, 0.f, 0.f, 0.f};
+            c[u][1] = c[u][0];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                c[u][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    av[u][k], __builtin_bit_cast(v8h, rq.qa[k]), c[u][0], 0, 0, 0);
+                c[u][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    av[u][k], __builtin_bit_cast(v8h, rq.qb[k]), c[u][1], 0, 0, 0);
+            }
+            // This tile's code registers are free: they take the next page's.
+            const int t = 2 * tp + u;
+            p.codes[t] = __builtin_amdgcn_raw_buffer_load_b128(nsrc, (16 * t + m) * 64 + 16 * g, 0,
+                                                               kStreamLoad);
+        }
+        // Issue order: the four table reads, the dequantization of both
+        // tiles, then their 16 MFMAs.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 200, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            mx0[i] = fmaxf(mx0[i], c0[i]);
-            mx1[i] = fmaxf(mx1[i], c1[i]);
+            mx0[i] = max3(mx0[i], c[0][0][i], c[1][0][i]);
+            mx1[i] = max3(mx1[i], c[0][1][i], c[1][1][i]);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    const float m0 = fmaxf(fmaxf(mx0[0], mx0[1]), fmaxf(mx0[2], mx0[3]));
-    const float m1 = fmaxf(fmaxf(mx1[0], mx1[1]), fmaxf(mx1[2], mx1[3]));
+    const float m0 = max3(mx0[0], mx0[1], __builtin_elementwise_maximum(mx0[2], mx0[3]));
+    const float m1 = max3(mx1[0], mx1[1], __builtin_elementwise_maximum(mx1[2], mx1[3]));
     // Join the four depth-chunk lanes of each row with two lane swaps: the
     // 32-lane swap pairs m0's halves in lanes 0..31 and m1's in 32..63, the
     // 16-lane swap finishes both.  Lane m then holds row m and lane 32 + m
     // row 16 + m (see store_row).
     const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(m0), __float_as_uint(m1), false,
                                                     false);
-    float x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+    float x = __builtin_elementwise_maximum(__uint_as_float(h[0]), __uint_as_float(h[1]));
     const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                     false);
-    x = fmaxf(x, __uint_as_float((lane & 16) ? q[0] : q[1]));
+    x = __builtin_elementwise_maximum(x, __uint_as_float((lane & 16) ? q[0] : q[1]));
     rmax = x;
-}
-
-// True when some scale byte of the page is NaN (0x7F or 0xFF): every dot
-// of that token is NaN, so the page's score is.
-__device__ __forceinline__ bool page_has_nan_scale(const PageRegs &p)
-{
-    bool nan = false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        nan |= has_nan_byte(p.scales[i]);
-    return __any(nan);
 }
 
 __global__ __launch_bounds__(256, 2) void score_decode_kernel(
@@ -398,17 +392,12 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
         const __amdgpu_buffer_rsrc_t nsrc = page_src(j + 1 < j1 ? j + 1 : j1, nxt_ok);
         uint32_t sc[8];
         unpack_scales(pr, stage, lane, m, g, sc);
-        const bool page_nan = page_has_nan_scale(pr);
         pr.scales = __builtin_amdgcn_raw_buffer_load_b128(nsrc, kCodeBytes + 16 * lane, 0, kStreamLoad);
         float v;
         score_page(pr, sc, lut, rq, nsrc, lane, m, g, v);
         // Lanes without a row have own = -1 and store nothing.
         if (cur_ok && j < rq.own) {
-            float s = (v + fabsf(v)) * 0.5f * rq.qs;
-            // The file is built without NaN semantics, so the NaN is written
-            // as its bit pattern (the canonical quiet NaN).
-            if (page_nan || rq.qnan)
-                s = __uint_as_float(0x7FC00000u);
+            const float s = (v + fabsf(v)) * 0.5f * rq.qs;
             scores[((int64_t)b * kDecodeRows + store_row(lane)) * width + j] = s;
         }
         cur_ok = nxt_ok;

@@ -96,14 +96,6 @@ __device__ __forceinline__ int lanes_set(uint64_t mask)
     return __builtin_popcount((uint32_t)mask) + __builtin_popcount((uint32_t)(mask >> 32));
 }
 
-// Orders this wave's LDS accesses before and after (a wave's LDS operations
-// execute in order; this stops the compiler from moving them across).
-__device__ __forceinline__ void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // The value of lane (lane ^ J).  J = 1, 2: quad permutes; J = 4: row shift
 // left or right by 4; J = 8: row rotate by 8; J = 16, 32: the gfx950 permlane
