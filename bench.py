@@ -18,6 +18,7 @@ duration against the HBM peak; `cpu_baseline` is the CPU oracle timed on a
 bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--pools P]
+  python bench.py --workload decode-tiny|decode-mtp|decode-ragged   # the other decode batches
   python bench.py --profile-pass     # short fixed sequence for rocprofv3 counter runs
   python bench.py --workload prefill # lightning-indexer prefill step (scores + top-16)
   python bench.py --workload dequant # NVFP4 gather-dequantize of the decode pages
@@ -101,13 +102,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--pools", type=int, default=4)
+    ap.add_argument("--pools", type=int, default=None,
+                    help="index-K pools rotated per step (default: per workload)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
-    ap.add_argument("--workload", choices=("decode", "prefill", "dequant", "nvfp4-prefill",
-                                           "mxfp8", "ragged-prefill"),
+    ap.add_argument("--workload", choices=("decode", "decode-tiny", "decode-mtp", "decode-ragged",
+                                           "prefill", "dequant", "nvfp4-prefill", "mxfp8",
+                                           "ragged-prefill"),
                     default="decode")
     return ap.parse_args()
 
@@ -326,6 +329,19 @@ def bench_nvfp4_prefill(args):
                              d.block_table.shape[1], keys)
     score_call = ps.prepare(ps.indexer_score_prefill, q, qs, keys.view(-1, 128)[:N], ones, scores)
     topk_call = ps.prepare(ps.topk16_select, scores, N, out)
+    if args.profile_pass:
+        # Fixed sequence for counter runs: a plain 1 GiB device copy (the
+        # calibration of FETCH_SIZE / WRITE_SIZE), then one launch of each call.
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        gather_call()
+        score_call()
+        topk_call()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_pass": True, "workload": "nvfp4-prefill", "copy_bytes": 1 << 30}),
+              flush=True)
+        return
     stream = torch.cuda.current_stream(dev)
 
     def step(i):
@@ -375,12 +391,29 @@ def bench_nvfp4_prefill(args):
         ones_h = np.ones(N, dtype=np.float32)
         t1 = time.perf_counter()
         n = 0
+        oracle_rows = []
         while n < T and time.perf_counter() - t1 < args.cpu_seconds:
             row = oracle.score_prefill_rows(d.q, d.q_scale, keys_ora, ones_h, [n])
             oracle.topk16(row)
+            oracle_rows.append(row[0])
             n += 1
         t_rows = time.perf_counter() - t1
         cpu_step = t_gather + t_rows * T / n
+        # The GPU's scores of the same rows against the oracle's: the count
+        # outside the plain bound 1e-6 + 1e-5 |oracle| (these cancelling dots
+        # do not all meet it), and outside the same bound on the size of the
+        # summed terms, M = sum_h q_scale sum_d |q k|.
+        got = scores[:n].cpu().numpy().astype(np.float64)
+        want = np.stack(oracle_rows).astype(np.float64)
+        qa = torch.from_numpy(d.q[:n]).view(torch.float8_e4m3fn).double().abs()
+        ka = torch.from_numpy(keys_ora).view(torch.float8_e4m3fn).double().abs()
+        mag = (torch.matmul(qa, ka.T.contiguous()) *
+               torch.from_numpy(d.q_scale[:n]).double().abs()[:, :, None]).sum(dim=1).numpy()
+        err = np.abs(got - want)
+        result["parity_sample"] = {
+            "rows": n, "scores": int(want.size),
+            "outside_plain_bound": int((err > 1e-6 + 1e-5 * np.abs(want)).sum()),
+            "outside_term_bound": int((err > 1e-6 + 1e-5 * np.maximum(np.abs(want), mag)).sum())}
         result["cpu_baseline"] = {
             "value": round(pairs / cpu_step / 1e9, 9), "unit": "G scores/s", "cores": 1,
             "kind": "oracle",
@@ -508,7 +541,7 @@ def bench_dequant(args):
     dev = torch.device("cuda", 0)
     d = workloads.long_decode()
     R, W = d.num_reqs, d.width
-    P = max(1, args.pools)
+    P = max(1, args.pools if args.pools is not None else 4)
     pools = [torch.from_numpy(d.kv_cache).to(dev)]
     gen = torch.Generator(device=dev)
     gen.manual_seed(1234)
@@ -610,6 +643,11 @@ def _oracle_decode_worker(w, workers, seconds):
     return n, time.perf_counter() - t0
 
 
+def host_cores() -> int:
+    """This process's CPU share, at most 16 (the share of one GPU)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def oracle_decode_parallel(d, qlen, W, pages, seconds):
     """The oracle's decode scoring rate (pages/s) over forked worker processes,
     one per host core of this process's share (at most 16).  Runs before the
@@ -620,7 +658,7 @@ def oracle_decode_parallel(d, qlen, W, pages, seconds):
     global _CPU_DECODE
     oracle.lib()                       # built and loaded once, before the fork
     _CPU_DECODE = (d, qlen, W, pages)
-    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    workers = min(host_cores(), pages)
     with mp.get_context("fork").Pool(workers) as pool:
         res = pool.starmap(_oracle_decode_worker, [(w, workers, seconds) for w in range(workers)])
     n = sum(r[0] for r in res)
@@ -628,18 +666,21 @@ def oracle_decode_parallel(d, qlen, W, pages, seconds):
     return n, t, workers
 
 
-def oracle_decode_legs(seconds):
-    """The oracle on the decode step, on one core and on one process per core:
-    pages per second of full-page scoring (all 32 rows of a page's request) and the
-    time of its top-16 over 128 rows of the step's width (seeded N(0,1) rows
-    with the rows' own pages as valid lengths and appended pages)."""
+def decode_pages_of(d):
+    return sum(min(max((int(s) - 1) // 128, 0), d.width) for s in d.seq_lens[:d.num_reqs])
+
+
+def oracle_decode_legs(d, seconds):
+    """The oracle on a decode step, on one core and on one process per core:
+    pages per second of full-page scoring (all 32 rows of a page's request)
+    and the time of its top-16 over the step's rows (seeded N(0,1) rows of the
+    step's width, with the rows' own pages as valid lengths and appended
+    pages)."""
     import numpy as np
 
     import oracle
-    import workloads
-    d = workloads.long_decode()
     W = d.width
-    pages = sum(min(max((int(s) - 1) // 128, 0), W) for s in d.seq_lens[:d.num_reqs])
+    pages = decode_pages_of(d)
     t0 = time.perf_counter()
     n = 0
     stride = 7   # pages spread over the step's requests
@@ -650,7 +691,8 @@ def oracle_decode_legs(seconds):
         n += 1
     t_cols = time.perf_counter() - t0
     rows = np.random.default_rng(7).standard_normal((d.num_reqs * 32, W)).astype(np.float32)
-    own = np.full(d.num_reqs * 32, W - 1, dtype=np.int32)
+    own = np.array([min(max((int(d.seq_lens[b]) - 1) // 128, 0), W) for b in range(d.num_reqs)
+                    for _ in range(32)], dtype=np.int32)
     t1 = time.perf_counter()
     oracle.topk16(rows, own, None, None, own)
     t_topk = time.perf_counter() - t1
@@ -658,42 +700,144 @@ def oracle_decode_legs(seconds):
     return {"pages": pages, "single": (n, t_cols), "parallel": (pn, pt, workers), "topk_s": t_topk}
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the indexer path "
-                          "has no multi-GPU mode", "n_gpus": args.gpus}), flush=True)
-        sys.exit(2)
+# ---------------------------------------------------------------------------
+# Timing helpers shared by the decode legs.
+# ---------------------------------------------------------------------------
 
-    # The parallel oracle leg of the decode step forks worker processes, so
-    # it runs before anything touches the GPU.
-    cpu_legs = None
-    if args.workload == "decode" and not args.no_cpu and not args.profile_pass:
-        cpu_legs = oracle_decode_legs(args.cpu_seconds)
+WINDOWS = 7            # repeated timed windows; the median is reported
+GRAPH_STEPS = 200      # steps captured per HIP graph
+GRAPH_REPLAYS = 15     # replays of it; the median is reported
 
+
+def stats(values):
+    v = sorted(values)
+    med = v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+    return {"median": med, "min": v[0], "max": v[-1],
+            "spread": (v[-1] - v[0]) / med if med > 0 else None}
+
+
+def windows(torch, stream, fn, n, count=WINDOWS):
+    """`count` windows of `n` back-to-back calls: ms per call of each."""
+    return [timed(torch, stream, fn, n) for _ in range(count)]
+
+
+def graph_replay_ms(torch, dev, make_step, steps=GRAPH_STEPS, replays=GRAPH_REPLAYS):
+    """Median ms per step of `steps` steps captured in one HIP graph and
+    replayed `replays` times (the pages' own timing method).  `make_step()`
+    builds the step's calls on the current (capture) stream."""
+    stream = torch.cuda.current_stream(dev)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        step = make_step()
+        step(0)                          # built and run once on the side stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            for i in range(steps):
+                step(i)
+    torch.cuda.synchronize()
+    g.replay()                           # warm
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(replays):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) / steps)
+    del g
+    return stats(per)
+
+
+def _sclk_mhz(torch):
+    """The GPU's current shader clock from sysfs (pp_dpm_sclk, the level
+    marked '*'), or None where it cannot be read."""
+    try:
+        p = torch.cuda.get_device_properties(0)
+        path = f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:" \
+               f"{p.pci_device_id:02x}.0/pp_dpm_sclk"
+        for line in open(path):
+            if "*" in line:
+                return float(line.split(":")[1].strip().split("M")[0].rstrip("*").strip())
+    except Exception:
+        return None
+    return None
+
+
+def machine_info(torch, sclk_samples):
+    """Which machine ran: host name, device identity, the peak shader clock
+    the runtime reports, and the shader clock read while timed work ran."""
+    import ctypes
+    import socket
+    p = torch.cuda.get_device_properties(0)
+    info = {"host": socket.gethostname(), "gpu": p.name, "arch": p.gcnArchName,
+            "compute_units": p.multi_processor_count, "uuid": str(p.uuid),
+            "pci": f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, 0) == 0:   # hipDeviceAttributeClockRate
+            info["peak_sclk_mhz"] = v.value / 1000.0
+    except OSError:
+        pass
+    got = [s for s in sclk_samples if s is not None]
+    info["sclk_mhz_during_timing"] = stats(got) if got else None
+    return info
+
+
+def timed_sampling_clock(torch, stream, fn, n, samples):
+    """timed(), reading the shader clock while the launched work runs."""
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(n):
+        fn(i)
+    stop.record(stream)
+    samples.append(_sclk_mhz(torch))
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / n
+
+
+# ---------------------------------------------------------------------------
+# Decode legs.
+# ---------------------------------------------------------------------------
+
+# Index-K pools per leg: enough that the pools rotated through a timed window
+# exceed the 256 MB last-level cache (at least 512 MB in total), except the
+# tiny batch, which is latency-bound and cache-resident by nature.
+DECODE_LEGS = {
+    "decode": ("long_decode", 4,
+               "long-context decode: 4 requests x 8 query slots x 4 index heads, 500,000-token "
+               "contexts (3,906 NVFP4 pages scored per request), then top-16 of 128 score rows"),
+    "decode-tiny": ("tiny_decode", 1,
+                    "tiny decode: 1 request, 1 query token x 4 index heads, 8,192-token context "
+                    "(63 NVFP4 pages scored), then top-16 of its 4 score rows"),
+    "decode-mtp": ("mtp_decode", 15,
+                   "MTP decode: 16 requests x 8 query slots x 4 index heads, 30,000-token "
+                   "contexts (234 NVFP4 pages scored per request), then top-16 of 512 rows"),
+    "decode-ragged": ("ragged_decode", 2,
+                      "ragged decode: 64 requests x 8 query slots x 4 index heads, contexts "
+                      "uniform in 1,000-172,032 tokens, rows of 1,344 columns, 8 padding "
+                      "requests, then top-16 of 2,048 rows"),
+}
+
+
+def bench_decode(args, leg, cpu_legs):
     import torch
-    torch.cuda.set_device(0)
-    if args.workload == "prefill":
-        return bench_prefill(args)
-    if args.workload == "dequant":
-        return bench_dequant(args)
-    if args.workload == "nvfp4-prefill":
-        return bench_nvfp4_prefill(args)
-    if args.workload == "mxfp8":
-        return bench_mxfp8(args)
-    if args.workload == "ragged-prefill":
-        return bench_ragged_prefill(args)
-
-    import numpy as np
 
     import page_scoring_top_amd as ps
     import workloads
 
     dev = torch.device("cuda", 0)
-    d = workloads.long_decode()
+    maker, default_pools, workload = DECODE_LEGS[leg]
+    d = getattr(workloads, maker)()
     R, W, qlen = d.num_reqs, d.width, d.qlen
-    P = max(1, args.pools)
+    Rt = d.q.shape[0]
+    P = max(1, args.pools if args.pools is not None else default_pools)
 
     # Index-K pools: pool 0 is the seeded host workload; the others are drawn
     # on the device with their own seeded generator (same distributions:
@@ -712,25 +856,36 @@ def main():
     seq = torch.from_numpy(d.seq_lens).to(dev)
     q = torch.from_numpy(d.q).to(dev)
     qs = torch.from_numpy(d.q_scale).to(dev)
-    scores = torch.zeros((R, 32, W), dtype=torch.float32, device=dev)
-    own = torch.zeros((R, 32), dtype=torch.int32, device=dev)
+    scores = torch.zeros((Rt, 32, W), dtype=torch.float32, device=dev)
+    own = torch.zeros((Rt, 32), dtype=torch.int32, device=dev)
     out = torch.zeros((R * 32, 16), dtype=torch.int32, device=dev)
 
-    score_calls = [ps.prepare(ps.indexer_score_decode, kv, bt, seq, q, qs, qlen, W, scores, own)
-                   for kv in pools]
-    topk_call = ps.prepare(ps.topk16_select, scores.view(R * 32, W), W, out,
-                           valid_len=own.view(-1), append_page=own.view(-1))
+    def make_calls():
+        sc = [ps.prepare(ps.indexer_score_decode, kv, bt, seq, q, qs, qlen, W, scores, own,
+                         num_reqs=R) for kv in pools]
+        tk = ps.prepare(ps.topk16_select, scores[:R].view(R * 32, W), W, out,
+                        valid_len=own[:R].view(-1), append_page=own[:R].view(-1))
+        return sc, tk
 
-    pages = sum(min(max((int(s) - 1) // 128, 0), W) for s in d.seq_lens[:R])
+    score_calls, topk_call = make_calls()
+    pages = decode_pages_of(d)
     kbytes = pages * 9216
-    stored = 32 * pages  # each of a request's 32 rows stores each of its scored pages
+    stored = 0
+    for b in range(R):
+        npg = min(max((int(d.seq_lens[b]) - 1) // 128, 0), W)
+        for slot in range(8):
+            i = slot - (8 - qlen)
+            pos = int(d.seq_lens[b]) - qlen + i
+            own_p = pos // 128 if i >= 0 and pos >= 0 else -1
+            stored += 4 * min(max(own_p, 0), npg)
     # Algorithmic bytes of one score launch: index-K pages, their block-table
     # entries, score writes, and per request q, q_scale, seq_len and own pages.
     algo_bytes = pages * (9216 + 4) + stored * 4 + R * (4096 + 128 + 4 + 128)
 
     if args.profile_pass:
         # Fixed sequence for counter runs: a plain 1 GiB device copy (the
-        # calibration of FETCH_SIZE / WRITE_SIZE), then one score launch per pool.
+        # calibration of FETCH_SIZE / WRITE_SIZE), then one score launch per
+        # pool and one top-16.
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
         b.copy_(a)
@@ -738,8 +893,8 @@ def main():
             c()
         topk_call()
         torch.cuda.synchronize()
-        print(json.dumps({"profile_pass": True, "copy_bytes": 1 << 30, "score_launches": P,
-                          "score_algo_bytes": algo_bytes}), flush=True)
+        print(json.dumps({"profile_pass": True, "workload": leg, "copy_bytes": 1 << 30,
+                          "score_launches": P, "score_algo_bytes": algo_bytes}), flush=True)
         return
 
     stream = torch.cuda.current_stream(dev)
@@ -753,18 +908,48 @@ def main():
         topk_call()
 
     K = args.steps
-    # The timed region: K whole steps back to back.
-    ms_per_step = timed(torch, stream, step, K)
-    # Each kernel's average launch duration, from runs of that kernel alone.
-    score_avg = timed(torch, stream, lambda i: score_calls[i % P](), K)
-    topk_avg = timed(torch, stream, lambda i: topk_call(), K)
+    clk = []
+    # The timed region: windows of K whole steps back to back; the median
+    # window is reported.
+    step_ms = stats([timed_sampling_clock(torch, stream, step, K, clk) for _ in range(WINDOWS)])
 
+    # The same step, and each kernel alone, as HIP-graph replays: no host
+    # launch cost between kernels, so a small kernel's time is its own (a
+    # back-to-back loop of small kernels measures the host's launch rate).
+    def make_step():
+        sc, tk = make_calls()
+
+        def graph_step(i):
+            sc[i % P]()
+            tk()
+        return graph_step
+
+    def make_score():
+        sc, _ = make_calls()
+        return lambda i: sc[i % P]()
+
+    def make_topk():
+        _, tk = make_calls()
+        return lambda i: tk()
+
+    graph_ms = graph_replay_ms(torch, dev, make_step)
+    score_ms = graph_replay_ms(torch, dev, make_score)
+    topk_ms = graph_replay_ms(torch, dev, make_topk)
+    # The score kernel alone, back to back with HIP events (host-launched).
+    score_loop_ms = stats([timed_sampling_clock(torch, stream, lambda i: score_calls[i % P](), K, clk)
+                           for _ in range(WINDOWS)])
+
+    ms_per_step = step_ms["median"]
     value = kbytes / (ms_per_step * 1e-3) / 1e9
-    achieved = algo_bytes / (score_avg * 1e-3) / 1e9
-    traffic = read_counters()
+    achieved = algo_bytes / (score_ms["median"] * 1e-3) / 1e9
+    traffic = read_counters(counters_file(leg))
+
+    def us(st):
+        return {k: (round(v * 1e3, 3) if k != "spread" else round(v, 4)) for k, v in st.items()}
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC if leg == "decode" else
+        f"index-K GB/s scored (frac of HBM peak) + top-16 rows/s, {leg[7:]} decode",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -777,16 +962,25 @@ def main():
         "dtype": "e4m3 values as f16, f32 accumulate",
         "data": "synthetic",
         "config": {
-            "workload": "long-context decode: 4 requests x 8 query slots x 4 index heads, "
-                        "500,000-token contexts (3,906 NVFP4 pages scored per request), "
-                        "then top-16 of 128 score rows",
-            "requests": R, "query_slots": 8, "heads": 4, "depth": 128, "seq_len": 500000,
+            "workload": workload,
+            "requests": R, "query_slots": 8, "qlen": qlen, "heads": 4, "depth": 128,
+            "seq_len": int(d.seq_lens[0]) if leg != "decode-ragged" else "1,000-172,032",
             "pages_scored": pages, "index_k_bytes": kbytes, "width": W, "index_k_pools": P,
             "parallelism": "single GPU",
         },
-        "top16_rows_per_s": round(R * 32 / (topk_avg * 1e-3), 1),
-        "kernels_us": {"indexer_score_decode": round(score_avg * 1e3, 3),
-                       "topk16_select": round(topk_avg * 1e3, 3)},
+        "top16_rows_per_s": round(R * 32 / (topk_ms["median"] * 1e-3), 1),
+        "timing": {
+            "windows": WINDOWS,
+            "step_us": us(step_ms),
+            "graph_replay_step_us": us(graph_ms),
+            "graph_replay": f"{GRAPH_STEPS} steps per HIP graph, median of {GRAPH_REPLAYS} "
+                            f"replays",
+            "graph_value": round(kbytes / (graph_ms["median"] * 1e-3) / 1e9, 2),
+        },
+        "kernels_us": {"indexer_score_decode": us(score_ms), "topk16_select": us(topk_ms),
+                       "timing": f"each kernel alone, {GRAPH_STEPS} launches per HIP graph, median of "
+                                 f"{GRAPH_REPLAYS} replays",
+                       "indexer_score_decode_host_loop": us(score_loop_ms)},
         "roofline": {
             "bound": "hbm",
             "kernel": "indexer_score_decode",
@@ -797,6 +991,7 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": algo_bytes,
         },
+        "machine": machine_info(torch, clk),
     }
 
     if cpu_legs is not None:
@@ -812,8 +1007,8 @@ def main():
             "kind": "oracle",
             "sample": f"the oracle in {workers} worker processes (one per host core of this "
                       f"process): {pn} full pages (32 rows each) in {pt:.2f} s, scaled to "
-                      f"{pages} pages, plus the single-core oracle top-16 of 128 rows of width "
-                      f"{W} ({t_topk:.3f} s); step estimate {stepn:.1f} s",
+                      f"{pages} pages, plus the single-core oracle top-16 of {R * 32} rows of "
+                      f"width {W} ({t_topk:.3f} s); step estimate {stepn:.2f} s",
         }
         result["cpu_baseline_1core"] = {
             "value": round(kbytes / step1 / 1e9, 6),
@@ -821,9 +1016,48 @@ def main():
             "cores": 1,
             "kind": "oracle",
             "sample": f"the oracle on one core: {n} full pages in {t_cols:.2f} s, scaled to "
-                      f"{pages} pages, plus the same top-16; step estimate {step1:.1f} s",
+                      f"{pages} pages, plus the same top-16; step estimate {step1:.2f} s",
         }
     print(json.dumps(result), flush=True)
+
+
+def counters_file(leg):
+    """The committed FETCH/WRITE counter summary of a decode leg."""
+    name = {"decode": "long", "decode-tiny": "tiny", "decode-mtp": "mtp",
+            "decode-ragged": "ragged"}[leg]
+    return os.path.join(ROOT, "profiles", f"score_decode_{name}_counters.txt")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the indexer path "
+                          "has no multi-GPU mode", "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    # The parallel oracle leg of a decode step forks worker processes, so it
+    # runs before anything touches the GPU.
+    cpu_legs = None
+    if args.workload in DECODE_LEGS and not args.no_cpu and not args.profile_pass:
+        import workloads
+        d = getattr(workloads, DECODE_LEGS[args.workload][0])()
+        cpu_legs = oracle_decode_legs(d, args.cpu_seconds)
+        del d
+
+    import torch
+    torch.cuda.set_device(0)
+    if args.workload == "prefill":
+        return bench_prefill(args)
+    if args.workload == "dequant":
+        return bench_dequant(args)
+    if args.workload == "nvfp4-prefill":
+        return bench_nvfp4_prefill(args)
+    if args.workload == "mxfp8":
+        return bench_mxfp8(args)
+    if args.workload == "ragged-prefill":
+        return bench_ragged_prefill(args)
+    return bench_decode(args, args.workload, cpu_legs)
 
 
 if __name__ == "__main__":

@@ -15,6 +15,10 @@ import bench  # noqa: E402
 
 COUNTERS = [
     (bench.COUNTERS_FILE, bench.SCORE_SOURCES, "score_decode.hip", 146070576),
+    (bench.counters_file("decode-mtp"), bench.SCORE_SOURCES, "score_decode.hip", 35068608),
+    (bench.counters_file("decode-ragged"), bench.SCORE_SOURCES, "score_decode.hip", 420807384),
+    # 63 pages: fixed per-launch reads (arguments, code) are a large share
+    (bench.counters_file("decode-tiny"), bench.SCORE_SOURCES, "score_decode.hip", None),
     (bench.MX_COUNTERS_FILE, bench.MX_SOURCES, "mxfp8.hip", 16384 * 2048 * 3 + 16384 * 2048 // 32),
     (bench.DQ_COUNTERS_FILE, bench.DQ_SOURCES, "dequant.hip", None),
 ]
