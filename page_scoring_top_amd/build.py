@@ -74,5 +74,19 @@ def build_library(verbose: bool = False) -> str:
     return LIB
 
 
+def build_test_probe() -> str:
+    """tests/probe/libmfma_probe.so: the test suite's matrix-instruction
+    accuracy probe (not part of the library)."""
+    src = os.path.join(ROOT, "tests", "probe", "mfma_accuracy.hip")
+    out = os.path.join(ROOT, "tests", "probe", "libmfma_probe.so")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", src, "-o", out + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     print(build_library(verbose="-v" in sys.argv))

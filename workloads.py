@@ -322,3 +322,29 @@ def injected_rows(seed: int, rows: int, width: int) -> TopkInputs:
         elif kind == 7:
             valid[r] = width + int(rng.integers(1, 1000))
     return TopkInputs(s, valid, fb, fe)
+
+
+# ---------------------------------------------------------------------------
+# Tiles for the matrix-instruction accuracy probe (tests/probe/).
+# ---------------------------------------------------------------------------
+
+def mfma_probe_tiles(seed: int, tiles: int):
+    """``(a, b)``, each ``[tiles, 16, 128]`` E4M3 bytes.  Even tiles: a's bytes
+    uniform over every finite E4M3 byte of either sign (keys of the whole
+    E4M3 range, as block-scaled NVFP4 keys reach), b = e4m3(N(0,1)) (queries).
+    Odd tiles cancel: the second half of each row repeats the first with a's
+    signs flipped, except for 16 depth positions redrawn at random (positive
+    finite bytes), so a dot
+    product is a small remainder of large terms."""
+    rng = _streams(seed)[_S_EXTRA]
+    a = rng.integers(0, 256, size=(tiles, 16, 128), dtype=np.uint8)
+    a[(a & 0x7F) == 0x7F] ^= 0x01            # no NaN bytes
+    b = e4m3_bytes_from_normal(rng, (tiles, 16, 128))
+    odd = np.arange(tiles) % 2 == 1
+    a[odd, :, 64:] = a[odd, :, :64] ^ 0x80
+    b[odd, :, 64:] = b[odd, :, :64]
+    for t in np.nonzero(odd)[0]:
+        for r in range(16):
+            pos = 64 + rng.permutation(64)[:16]
+            a[t, r, pos] = rng.integers(0, 0x7F, size=16, dtype=np.uint8)
+    return a, b
