@@ -184,3 +184,22 @@ def test_out_of_range_page_ids_are_skipped():
                           np.full(got.shape, CANARY_F32, np.float32)[~m].view(np.int32)), \
         "a column with an out-of-range id, or outside the stored region, was written"
     assert_scores_close(got[m], want[m], "bad ids")
+
+
+def test_most_requests_in_one_call():
+    """65,535 requests, the most one call takes (one grid row each): every
+    request writes its own pages, 1 in 64 has two scored pages and the rest
+    none; the pages are drawn from a shared pool of 64."""
+    R, W = 65535, 2
+    rng = np.random.default_rng(41)
+    seq = np.where(np.arange(R) % 64 == 5, 300, 100).astype(np.int32)
+    base = workloads.decode_inputs("max-reqs-pool", 41, [300], qlen=8, width=W, pool_pages=64)
+    kv = base.kv_cache
+    bt = rng.integers(0, kv.shape[0], size=(R, W), dtype=np.int32)
+    q = workloads.e4m3_bytes_from_normal(rng, (R, 8, 4, 128))
+    qs = rng.uniform(0.5, 2.0, size=(R, 8, 4)).astype(np.float32)
+    d = workloads.DecodeInputs("max-reqs", kv, bt, seq, q, qs, 8, W, R)
+    announce("decode 65,535 requests")
+    s, own = run_decode(d)
+    n = check_full(d, s, own, pooled=True)
+    assert n == (R // 64 + (1 if R % 64 > 5 else 0)) * 32 * 2

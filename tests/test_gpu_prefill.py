@@ -75,3 +75,14 @@ def test_big_config_rows_of_every_group():
     rows = [8 * g + (g % 8) for g in range(256)]
     want = oracle_pool.score_prefill_rows(p.q, p.q_scale, p.k, p.k_scale, rows)
     assert_scores_close(got[rows], want, "big prefill")
+
+
+def test_most_heads():
+    """224 heads, the most one call takes (a work-group holds one token's
+    query rows as f16 in its LDS)."""
+    p = workloads.prefill_inputs("max-heads", 224, 5, 224, 300)
+    announce("prefill T=5 H=224 N=300")
+    got = gpu_prefill(p, ld=301)
+    want = oracle.score_prefill(p.q, p.q_scale, p.k, p.k_scale)
+    assert_scores_close(got[:, :300], want, "H=224")
+    assert (got[:, 300:].view(np.int32) == CANARY_F32.view(np.int32)).all()

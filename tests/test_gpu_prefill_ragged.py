@@ -117,3 +117,20 @@ def test_big_batch_rows_of_every_wave():
 
     for (s, t, c), want in zip(pieces, oracle_pool.map_pieces(one, pieces, "ragged rows")):
         assert_scores_close(got[t, :c], want, f"row {t}")
+
+
+def test_most_sequences_in_one_call():
+    """65,535 sequences, the most one call takes (one grid slice each): most
+    have no query, 1 in 128 has two queries over a short context."""
+    S = 65535
+    q_lens = np.where(np.arange(S) % 128 == 3, 2, 0)
+    k_lens = np.where(np.arange(S) % 128 == 3, 40, 3)
+    p, q_start, k_start, k_len = ragged_batch(52, list(q_lens), list(k_lens), 4, gap=0)
+    width = 42
+    announce("ragged prefill 65,535 sequences")
+    got, row_len, ids = run(p, q_start, k_start, k_len, width, width)
+    want, want_len = oracle.score_prefill_ragged(p.q, p.q_scale, p.k, p.k_scale, q_start, k_start,
+                                                 k_len, width)
+    assert np.array_equal(row_len, want_len)
+    assert_scores_close(got, want, "65,535 sequences")
+    assert np.array_equal(ids, oracle.topk16(got, valid_len=want_len))
