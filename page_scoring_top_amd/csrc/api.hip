@@ -116,7 +116,7 @@ int indexer_score_prefill_ragged(const uint8_t *q, const float *q_scale, const u
         return PAGESCORE_EINVAL;
     return launch_status(pagescore::launch_score_prefill_ragged(
         q, q_scale, k, k_scale, T, H, N, num_seqs, q_start, k_start, k_len, max_q, width, scores, ld,
-        row_len, (hipStream_t)stream));
+        row_len, current_device_cus(), (hipStream_t)stream));
 }
 
 int topk16_select(const float *scores, int64_t row_stride, int32_t num_rows, int32_t width,

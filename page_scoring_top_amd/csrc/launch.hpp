@@ -42,7 +42,7 @@ hipError_t launch_score_prefill_ragged(const uint8_t *q, const float *q_scale, c
                                        int32_t num_seqs, const int32_t *q_start,
                                        const int32_t *k_start, const int32_t *k_len, int32_t max_q,
                                        int32_t width, float *scores, int64_t ld, int32_t *row_len,
-                                       hipStream_t stream);
+                                       int num_cus, hipStream_t stream);
 
 hipError_t launch_topk16(const float *scores, int64_t row_stride, int32_t num_rows, int32_t width,
                          const int32_t *valid_len, const int32_t *force_begin,

@@ -194,14 +194,22 @@ constexpr int64_t kPackMaxLd = 1 << 24;                       // 16 rows of scor
 // keys.  Score columns are relative to the sequence's first key; a
 // work-group computes only the key chunks some of its queries see and fills
 // the rest of its column range with -inf.
+typedef uint8_t KeyChunks[kChunkBufs][kChunkKeys * kKeyRowBytes];
+typedef float KeyScales[kChunkBufs][kChunkKeys];
+
+// One unit of work-group work: the queries [tb, tb + kTokPerGroup) of
+// sequence sq (the whole batch when not causal) against columns [kb, ke)
+// (ke clamped to the row width); first_split: the unit holding column 0
+// writes row_len.  kbuf / ks_lds: the work-group's LDS key chunks.  Every
+// thread of the work-group calls it with the same arguments.
 template <int kHT, bool kPack, bool kCausal>
-__global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel(
-    const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
-    const uint8_t *__restrict__ k, const float *__restrict__ k_scale, int32_t T, int32_t H,
-    int32_t N, int32_t keys_per_group, float *__restrict__ scores, int64_t ld, RaggedBatch rb)
+__device__ __forceinline__ void prefill_unit(
+    KeyChunks &kbuf, KeyScales &ks_lds, const uint8_t *__restrict__ q,
+    const float *__restrict__ q_scale, const uint8_t *__restrict__ k,
+    const float *__restrict__ k_scale, int32_t T, int32_t H, int32_t N,
+    float *__restrict__ scores, int64_t ld, const RaggedBatch &rb, int sq, int tb, int kb,
+    int64_t ke_in, bool first_split)
 {
-    __shared__ __align__(16) uint8_t kbuf[kChunkBufs][kChunkKeys * kKeyRowBytes];
-    __shared__ float ks_lds[kChunkBufs][kChunkKeys];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lane = tid % kWave;
@@ -215,7 +223,6 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
     int64_t row0 = 0, row_end = T;
     int32_t klen = N, width = N;
     if constexpr (kCausal) {
-        const int sq = blockIdx.z;
         int64_t a0 = rb.q_start[sq], a1 = rb.q_start[sq + 1];
         a0 = a0 < 0 ? 0 : (a0 > T ? T : a0);
         a1 = a1 < a0 ? a0 : (a1 > T ? T : a1);
@@ -232,15 +239,13 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
         k_scale += (k0 < 0 || k0 > N ? 0 : k0);
     }
     const int q_len = (int)(row_end - row0);
-    const int tb = blockIdx.x * kTokPerGroup;
     if (tb >= q_len)
         return;
     const int iw = tb + wave * kTokPerWave;                 // the wave's first query of the sequence
     const int64_t t = row0 + iw;
     const int tok_rows = iw >= q_len ? 0 : (q_len - iw < kTokPerWave ? q_len - iw : kTokPerWave);
     const bool tok_ok = tok_rows > 0;
-    const int kb = blockIdx.y * keys_per_group;
-    const int ke = kb + keys_per_group < width ? kb + keys_per_group : width;
+    const int ke = (int)(ke_in < width ? ke_in : width);
     // Visible keys of query i of the sequence (all of them without the mask).
     auto visible = [&](int i) {
         if constexpr (!kCausal)
@@ -254,7 +259,7 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
         const int last = tb + kTokPerGroup < q_len ? tb + kTokPerGroup - 1 : q_len - 1;
         const int cmax = visible(last);
         kc = cmax < kb ? kb : (cmax < ke ? cmax : ke);
-        if (blockIdx.y == 0 && rb.row_len != nullptr && lane < tok_rows)
+        if (first_split && rb.row_len != nullptr && lane < tok_rows)
             rb.row_len[t + lane] = visible(iw + lane);
     }
     const int chunks = (kc - kb + kChunkKeys - 1) / kChunkKeys;
@@ -505,6 +510,124 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
     }
 }
 
+// One unit per work-group: grid (token groups, key splits, sequences).
+template <int kHT, bool kPack, bool kCausal>
+__global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel(
+    const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
+    const uint8_t *__restrict__ k, const float *__restrict__ k_scale, int32_t T, int32_t H,
+    int32_t N, int32_t keys_per_group, float *__restrict__ scores, int64_t ld, RaggedBatch rb)
+{
+    __shared__ __align__(16) KeyChunks kbuf;
+    __shared__ KeyScales ks_lds;
+    constexpr int kTokPerGroup = kH64Waves * (kPack ? 8 * kHT : 1);
+    const int kb = blockIdx.y * keys_per_group;
+    prefill_unit<kHT, kPack, kCausal>(kbuf, ks_lds, q, q_scale, k, k_scale, T, H, N, scores, ld, rb,
+                                      blockIdx.z, blockIdx.x * kTokPerGroup, kb,
+                                      (int64_t)kb + keys_per_group, blockIdx.y == 0);
+}
+
+// Chunks a causal query group computes: its last query's visible keys
+// (clamped as prefill_unit clamps them) in 128-key chunks.
+__device__ __forceinline__ int64_t group_chunks(int32_t q_len, int32_t klen, int32_t width, int x)
+{
+    const int last = (x + 1) * kH64Waves - 1 < q_len ? (x + 1) * kH64Waves - 1 : q_len - 1;
+    int64_t c = (int64_t)klen - q_len + last + 1;
+    const int64_t hi = klen < width ? klen : width;
+    c = c > hi ? hi : (c < 0 ? 0 : c);
+    return (c + kChunkKeys - 1) / kChunkKeys;
+}
+
+// The ragged causal batch with a balanced schedule (one token per wave):
+// the batch's work is the list of (sequence, group of eight queries, chunk
+// of 128 visible keys) in that order, and work-group b of G takes positions
+// [W b / G, W (b + 1) / G) of it, W its length -- a share equal to within
+// one chunk, whatever the sequences' lengths.  A share is a few segments of
+// consecutive chunks of one query group; each runs as a prefill_unit over
+// the segment's columns (the group's last segment also fills its rows with
+// -inf up to the width).  A group with no visible key is a zero-chunk
+// segment of the work-group whose share holds its list position (the last
+// work-group for one past the end).  Every thread walks the list
+// identically, so the work-group's barriers match.
+template <int kHT>
+__global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_balanced_kernel(
+    const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
+    const uint8_t *__restrict__ k, const float *__restrict__ k_scale, int32_t T, int32_t H,
+    int32_t N, int32_t num_seqs, float *__restrict__ scores, int64_t ld, RaggedBatch rb)
+{
+    __shared__ __align__(16) KeyChunks kbuf;
+    __shared__ KeyScales ks_lds;
+    const int lane = threadIdx.x % kWave;
+    // Query and key counts of sequence s, clamped as prefill_unit clamps them.
+    auto seq_dims = [&](int s, int32_t &q_len, int32_t &klen) {
+        int64_t a0 = rb.q_start[s], a1 = rb.q_start[s + 1];
+        a0 = a0 < 0 ? 0 : (a0 > T ? T : a0);
+        a1 = a1 < a0 ? a0 : (a1 > T ? T : a1);
+        const int64_t k0 = rb.k_start[s];
+        int64_t kl = rb.k_len[s];
+        kl = (k0 < 0 || k0 > N) ? 0 : (kl > N - k0 ? N - k0 : (kl < 0 ? 0 : kl));
+        q_len = __builtin_amdgcn_readfirstlane((int32_t)(a1 - a0));
+        klen = __builtin_amdgcn_readfirstlane((int32_t)kl);
+    };
+    // Chunks of sequence s: the lanes take its groups in turn and a wave sum
+    // joins them.
+    auto seq_chunks = [&](int32_t q_len, int32_t klen) {
+        const int groups = (q_len + kH64Waves - 1) / kH64Waves;
+        int64_t mine = 0;
+        for (int x = lane; x < groups; x += kWave)
+            mine += group_chunks(q_len, klen, rb.width, x);
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1)
+            mine += __shfl_xor(mine, d);
+        return (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)mine) |
+               ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)(mine >> 32)) << 32);
+    };
+    int64_t W = 0;
+    for (int s = 0; s < num_seqs; ++s) {
+        int32_t q_len, klen;
+        seq_dims(s, q_len, klen);
+        W += seq_chunks(q_len, klen);
+    }
+    const int64_t G = gridDim.x, b = blockIdx.x;
+    const int64_t start = W * b / G, end = W * (b + 1) / G;
+    const bool last_block = b == G - 1;
+    // Walk the list to this share: whole sequences first, then groups.
+    int64_t pos = 0;
+    for (int s = 0; s < num_seqs && pos <= end; ++s) {
+        int32_t q_len, klen;
+        seq_dims(s, q_len, klen);
+        const int groups = (q_len + kH64Waves - 1) / kH64Waves;
+        if (groups == 0)
+            continue;
+        const int64_t tot = seq_chunks(q_len, klen);
+        // A sequence entirely before the share is skipped (one entirely
+        // after it ends the walk, by the loop condition); a sequence ending
+        // exactly at `start` may still hold zero-chunk groups at `start`.
+        if (pos + tot < start) {
+            pos += tot;
+            continue;
+        }
+        for (int x = 0; x < groups; ++x) {
+            const int64_t nc = group_chunks(q_len, klen, rb.width, x);
+            // This group's list positions [pos, pos + nc) inside [start, end),
+            // or a zero-chunk group at a position this share owns.
+            const int64_t a = pos > start ? pos : start;
+            const int64_t e = pos + nc < end ? pos + nc : end;
+            const bool owns_empty = nc == 0 && ((pos >= start && pos < end) || (last_block && pos >= W));
+            if (a < e || owns_empty) {
+                const int64_t ca = nc == 0 ? 0 : a - pos, cb = nc == 0 ? 0 : e - pos;
+                const int64_t ke = cb == nc ? (int64_t)rb.width : cb * kChunkKeys;
+                prefill_unit<kHT, false, true>(kbuf, ks_lds, q, q_scale, k, k_scale, T, H, N, scores,
+                                               ld, rb, s, x * kH64Waves, (int)(ca * kChunkKeys), ke,
+                                               ca == 0);
+                __syncthreads();   // the next unit rewrites the LDS chunks
+            }
+            pos += nc;
+            if (pos > end || (pos == end && !last_block && nc > 0))
+                break;
+        }
+    }
+}
+
 }  // namespace
 
 static_assert(kPrefillMaxHeads * ((kRowHalves * 2) + 4) <= kLdsBytes,
@@ -516,8 +639,11 @@ namespace {
 // `num_seqs` work-groups, with columns [0, width) split in whole chunks of
 // 128 keys (at most 2^20 per work-group) so the grid holds about one
 // work-group per compute unit.
+// Sequences up to which a causal launch of the one-token path takes the
+// balanced schedule (each work-group walks the whole sequence list once).
+constexpr int32_t kBalancedMaxSeqs = 256;
 // Work-groups a causal launch of the one-token path aims at (about four
-// per compute unit).
+// per compute unit) when it takes the grid instead.
 constexpr int64_t kCausalTargetGroups = 1024;
 
 template <bool kCausal>
@@ -574,12 +700,25 @@ hipError_t launch_score_prefill_ragged(const uint8_t *q, const float *q_scale, c
                                        int32_t num_seqs, const int32_t *q_start,
                                        const int32_t *k_start, const int32_t *k_len, int32_t max_q,
                                        int32_t width, float *scores, int64_t ld, int32_t *row_len,
-                                       hipStream_t stream)
+                                       int num_cus, hipStream_t stream)
 {
     static_assert(kRaggedMaxHeads == kSmallHeads, "the ragged batch runs the small-head kernel only");
     if (H > kSmallHeads || num_seqs > 65535)
         return hipErrorInvalidValue;
     const RaggedBatch rb{q_start, k_start, k_len, row_len, width};
+    // One token per wave over a few sequences: the balanced schedule, one
+    // work-group per compute unit (the kernel's registers allow one).
+    const bool pack = H <= kPackHeads && ld <= kPackMaxLd;
+    if (!pack && num_seqs <= kBalancedMaxSeqs) {
+        const dim3 grid((uint32_t)(num_cus > 0 ? num_cus : 256)), block(kH64Waves * kWave);
+        if (H <= 32)
+            hipLaunchKernelGGL(score_prefill_balanced_kernel<1>, grid, block, 0, stream, q, q_scale,
+                               k, k_scale, T, H, N, num_seqs, scores, ld, rb);
+        else
+            hipLaunchKernelGGL(score_prefill_balanced_kernel<2>, grid, block, 0, stream, q, q_scale,
+                               k, k_scale, T, H, N, num_seqs, scores, ld, rb);
+        return hipGetLastError();
+    }
     return launch_h64<true>(q, q_scale, k, k_scale, T, H, N, scores, ld, max_q, width, num_seqs, rb,
                             stream);
 }
