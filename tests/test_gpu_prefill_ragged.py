@@ -51,6 +51,11 @@ CASES = [
     ([1, 37, 130, 5, 0, 64, 150, 10], [1, 1000, 130, 3000, 200, 64, 2000, 3]),
     ([129], [129]),
     ([3, 2], [5000, 7]),
+    # query groups that see no key (40 queries over 5 keys; a sequence with no
+    # keys), a single query, and sequences of many chunks, split over the
+    # shares of several work-groups of the balanced schedule (57 chunks in
+    # all, fewer than the work-groups, so most shares are one chunk or none)
+    ([40, 24, 8, 1, 17], [5, 1500, 0, 129, 700]),
 ]
 
 
