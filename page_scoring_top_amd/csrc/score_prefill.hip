@@ -21,8 +21,11 @@
 // epilogue of each key tile interleaved into the next tile's MFMAs: one
 // token per wave, or up to four heads of 8 or 16 tokens packed into the
 // MFMA rows (the module description packs (token, head) pairs the same way,
-// on the other operand).  The same kernel runs the ragged causal batch of
-// indexer_score_prefill_ragged.  More heads take the general kernel: a
+// on the other operand).  The same per-unit code runs the ragged causal batch
+// of indexer_score_prefill_ragged, either one unit per work-group of a grid
+// or, for up to 256 sequences with one token per wave, as a balanced
+// schedule: one work-group per compute unit, each taking an equal share of
+// the batch's chunks.  More heads take the general kernel: a
 // work-group converts a few tokens' query rows once into LDS, and each wave
 // takes 32-key tiles, converts them into its B registers and runs every
 // token of the group against them.
@@ -186,7 +189,7 @@ constexpr int64_t kPackMaxLd = 1 << 24;                       // 16 rows of scor
 // tile ht is then head i % 4 of token 8 ht + 2 (i / 4) + half, so the head
 // sum of a (token, key) score is four elements of one lane, and a lane
 // stores 4 kHT scores per tile.
-// kCausal: a ragged batch of sequences (grid z), each query row masked
+// kCausal: a ragged batch of sequences (sq), each query row masked
 // causally and its row filled with -inf past its visible keys.  Sequence s
 // owns query rows [q_start[s], q_start[s+1]) and keys k_start[s] ..
 // + k_len[s]; its queries are the last q_len tokens of its context, so
