@@ -721,10 +721,9 @@ def windows(torch, stream, fn, n, count=WINDOWS):
     return [timed(torch, stream, fn, n) for _ in range(count)]
 
 
-def graph_replay_ms(torch, dev, make_step, steps=GRAPH_STEPS, replays=GRAPH_REPLAYS):
-    """Median ms per step of `steps` steps captured in one HIP graph and
-    replayed `replays` times (the pages' own timing method).  `make_step()`
-    builds the step's calls on the current (capture) stream."""
+def _capture(torch, dev, make_step, steps):
+    """One HIP graph holding `steps` steps; `make_step()` builds the step's
+    calls on the current (capture) stream."""
     stream = torch.cuda.current_stream(dev)
     side = torch.cuda.Stream(dev)
     side.wait_stream(stream)
@@ -737,6 +736,14 @@ def graph_replay_ms(torch, dev, make_step, steps=GRAPH_STEPS, replays=GRAPH_REPL
             for i in range(steps):
                 step(i)
     torch.cuda.synchronize()
+    return g
+
+
+def graph_replay_ms(torch, dev, make_step, steps=GRAPH_STEPS, replays=GRAPH_REPLAYS):
+    """Median ms per step of `steps` steps captured in one HIP graph and
+    replayed `replays` times (the pages' own timing method)."""
+    stream = torch.cuda.current_stream(dev)
+    g = _capture(torch, dev, make_step, steps)
     g.replay()                           # warm
     torch.cuda.synchronize()
     per = []
@@ -765,6 +772,63 @@ def _sclk_mhz(torch):
     except Exception:
         return None
     return None
+
+
+def _hwmon(torch, name):
+    """A value of the GPU's hwmon node (microwatts for power files), or None."""
+    import glob
+    try:
+        p = torch.cuda.get_device_properties(0)
+        base = f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:" \
+               f"{p.pci_device_id:02x}.0/hwmon/hwmon*/{name}"
+        for path in sorted(glob.glob(base)):
+            return float(open(path).read().split()[0])
+    except Exception:
+        return None
+    return None
+
+
+def sustained_power(torch, dev, make_step, seconds=1.0, steps=GRAPH_STEPS):
+    """Board power while the step runs back to back for about `seconds`
+    (HIP-graph replays, no host gaps), read from hwmon every 2 ms on a host
+    thread; the first quarter of the samples (ramp) is dropped.  Returns the
+    median power, the board's power cap and the time per step meanwhile, or
+    None where the power cannot be read."""
+    import threading
+    import time
+    if _hwmon(torch, "power1_input") is None:
+        return None
+    stream = torch.cuda.current_stream(dev)
+    g = _capture(torch, dev, make_step, steps)
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    per_replay = max(time.perf_counter() - t0, 1e-4)
+    n = max(4, int(seconds / per_replay))
+    samples, run = [], [True]
+
+    def sample():
+        while run[0]:
+            samples.append(_hwmon(torch, "power1_input"))
+            time.sleep(0.002)
+    th = threading.Thread(target=sample)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    th.start()
+    a.record(stream)
+    for _ in range(n):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    run[0] = False
+    th.join()
+    del g
+    got = [v for v in samples[len(samples) // 4:] if v is not None]
+    cap = _hwmon(torch, "power1_cap")
+    return {"power_w": round(stats(got)["median"] / 1e6, 1) if got else None,
+            "power_cap_w": round(cap / 1e6, 1) if cap else None,
+            "us_per_step": round(a.elapsed_time(b) * 1e3 / (n * steps), 3),
+            "seconds": round(a.elapsed_time(b) / 1e3, 3), "samples": len(got)}
 
 
 def machine_info(torch, sclk_samples):
@@ -935,6 +999,8 @@ def bench_decode(args, leg, cpu_legs):
     graph_ms = graph_replay_ms(torch, dev, make_step)
     score_ms = graph_replay_ms(torch, dev, make_score)
     topk_ms = graph_replay_ms(torch, dev, make_topk)
+    # The score kernel for about a second, with the board's power read meanwhile.
+    score_power = sustained_power(torch, dev, make_score)
     # The score kernel alone, back to back with HIP events (host-launched).
     score_loop_ms = stats([timed_sampling_clock(torch, stream, lambda i: score_calls[i % P](), K, clk)
                            for _ in range(WINDOWS)])
@@ -980,7 +1046,8 @@ def bench_decode(args, leg, cpu_legs):
         "kernels_us": {"indexer_score_decode": us(score_ms), "topk16_select": us(topk_ms),
                        "timing": f"each kernel alone, {GRAPH_STEPS} launches per HIP graph, median of "
                                  f"{GRAPH_REPLAYS} replays",
-                       "indexer_score_decode_host_loop": us(score_loop_ms)},
+                       "indexer_score_decode_host_loop": us(score_loop_ms),
+                       "indexer_score_decode_sustained": score_power},
         "roofline": {
             "bound": "hbm",
             "kernel": "indexer_score_decode",
