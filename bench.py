@@ -47,6 +47,8 @@ MX_COUNTERS_FILE = os.path.join(ROOT, "profiles", "mxfp8_quant_counters.txt")
 MX_SOURCES = ["csrc/mxfp8.hip", "csrc/device_common.hpp", "csrc/nvfp4_lut.hpp"]
 DQ_COUNTERS_FILE = os.path.join(ROOT, "profiles", "nvfp4_dequant_counters.txt")
 DQ_SOURCES = ["csrc/dequant.hip", "csrc/device_common.hpp", "csrc/nvfp4_lut.hpp"]
+PREFILL_SOURCES = ["csrc/score_prefill.hip", "csrc/device_common.hpp", "csrc/nvfp4_lut.hpp"]
+TOPK_SOURCES = ["csrc/topk16.hip", "csrc/device_common.hpp", "csrc/nvfp4_lut.hpp"]
 
 
 def _compile_flags(source):
@@ -163,9 +165,11 @@ def bench_prefill(args):
         score_call()
         topk_call()
 
-    ms_per_step = timed(torch, stream, step, K)
-    score_ms = timed(torch, stream, lambda i: score_call(), K)
-    topk_ms = timed(torch, stream, lambda i: topk_call(), K)
+    clk = []
+    step_st = windowed(torch, stream, step, K, clk)
+    score_st = windowed(torch, stream, lambda i: score_call(), K, clk)
+    topk_st = windowed(torch, stream, lambda i: topk_call(), K, clk)
+    ms_per_step, score_ms, topk_ms = step_st["median"], score_st["median"], topk_st["median"]
     flops = 2.0 * T * N * H * 128          # the contraction (the epilogue is not counted)
     achieved = flops / (score_ms * 1e-3) / 1e12
     result = {
@@ -180,12 +184,15 @@ def bench_prefill(args):
                                "against 16,384 keys, then top-16 of 2,048 rows",
                    "tokens": T, "heads": H, "keys": N, "depth": 128, "parallelism": "single GPU"},
         "top16_rows_per_s": round(T / (topk_ms * 1e-3), 1),
-        "kernels_us": {"indexer_score_prefill": round(score_ms * 1e3, 3),
-                       "topk16_select": round(topk_ms * 1e3, 3)},
+        "timing": {"windows": WINDOWS, "step_us": us_stats(step_st)},
+        "kernels_us": {"indexer_score_prefill": us_stats(score_st),
+                       "topk16_select": us_stats(topk_st),
+                       "timing": f"each kernel alone, median of {WINDOWS} windows of {K} launches"},
         "roofline": {"bound": "mfma", "kernel": "indexer_score_prefill",
                      "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                      "traffic": None, "algorithmic_flops_per_launch": flops},
+        "machine": machine_info(torch, clk),
     }
     if not args.no_cpu:
         import oracle
@@ -243,9 +250,11 @@ def bench_ragged_prefill(args):
         step(i)
     torch.cuda.synchronize()
     K = args.steps
-    ms_per_step = timed(torch, stream, step, K)
-    score_ms = timed(torch, stream, lambda i: score_call(), K)
-    topk_ms = timed(torch, stream, lambda i: topk_call(), K)
+    clk = []
+    step_st = windowed(torch, stream, step, K, clk)
+    score_st = windowed(torch, stream, lambda i: score_call(), K, clk)
+    topk_st = windowed(torch, stream, lambda i: topk_call(), K, clk)
+    ms_per_step, score_ms, topk_ms = step_st["median"], score_st["median"], topk_st["median"]
     # Visible (query, key) pairs: sequence s's query i sees k_len - q_len + i + 1 keys.
     pairs = 0
     for s in range(len(d.k_len)):
@@ -267,12 +276,15 @@ def bench_ragged_prefill(args):
                                "-inf tail fill, then top-16 of 2,048 rows",
                    "tokens": T, "heads": H, "width": W, "visible_pairs": pairs,
                    "parallelism": "single GPU"},
-        "kernels_us": {"indexer_score_prefill_ragged": round(score_ms * 1e3, 3),
-                       "topk16_select": round(topk_ms * 1e3, 3)},
+        "timing": {"windows": WINDOWS, "step_us": us_stats(step_st)},
+        "kernels_us": {"indexer_score_prefill_ragged": us_stats(score_st),
+                       "topk16_select": us_stats(topk_st),
+                       "timing": f"each kernel alone, median of {WINDOWS} windows of {K} launches"},
         "roofline": {"bound": "mfma", "kernel": "indexer_score_prefill_ragged",
                      "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                      "traffic": None, "algorithmic_flops_per_launch": flops},
+        "machine": machine_info(torch, clk),
     }
     if not args.no_cpu:
         import oracle
@@ -353,10 +365,12 @@ def bench_nvfp4_prefill(args):
         step(i)
     torch.cuda.synchronize()
     K = args.steps
-    ms_per_step = timed(torch, stream, step, K)
-    gather_ms = timed(torch, stream, lambda i: gather_call(), K)
-    score_ms = timed(torch, stream, lambda i: score_call(), K)
-    topk_ms = timed(torch, stream, lambda i: topk_call(), K)
+    clk = []
+    step_st = windowed(torch, stream, step, K, clk)
+    gather_st = windowed(torch, stream, lambda i: gather_call(), K, clk)
+    score_st = windowed(torch, stream, lambda i: score_call(), K, clk)
+    topk_st = windowed(torch, stream, lambda i: topk_call(), K, clk)
+    ms_per_step, score_ms = step_st["median"], score_st["median"]
     # Score kernel: queries, scales and keys read once, every score written once.
     algo = T * H * (128 + 4) + N * (128 + 4) + T * N * 4
     achieved = algo / (score_ms * 1e-3) / 1e9
@@ -372,13 +386,16 @@ def bench_nvfp4_prefill(args):
         "config": {"workload": "NVFP4 prefill: 512 pages (65,536-token context) gathered to E4M3, "
                                "2,048 tokens x 4 heads x depth 128 scored, top-16 of 2,048 rows",
                    "tokens": T, "heads": H, "keys": N, "pages": P, "parallelism": "single GPU"},
-        "kernels_us": {"nvfp4_index_k_dequant": round(gather_ms * 1e3, 3),
-                       "indexer_score_prefill": round(score_ms * 1e3, 3),
-                       "topk16_select": round(topk_ms * 1e3, 3)},
+        "timing": {"windows": WINDOWS, "step_us": us_stats(step_st)},
+        "kernels_us": {"nvfp4_index_k_dequant": us_stats(gather_st),
+                       "indexer_score_prefill": us_stats(score_st),
+                       "topk16_select": us_stats(topk_st),
+                       "timing": f"each kernel alone, median of {WINDOWS} windows of {K} launches"},
         "roofline": {"bound": "hbm", "kernel": "indexer_score_prefill",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": algo},
+        "machine": machine_info(torch, clk),
     }
     if not args.no_cpu:
         import numpy as np
@@ -462,7 +479,9 @@ def bench_mxfp8(args):
     for i in range(args.warmup):
         calls[i % P]()
     torch.cuda.synchronize()
-    ms = timed(torch, stream, lambda i: calls[i % P](), args.steps)
+    clk = []
+    st = windowed(torch, stream, lambda i: calls[i % P](), args.steps, clk)
+    ms = st["median"]
 
     # Decode batch in a graph.
     dr = 128
@@ -507,13 +526,15 @@ def bench_mxfp8(args):
         "config": {"workload": "MXFP8 (E4M3 + E8M0 per 32) quantization of 16,384 x 2,048 bf16 "
                                "attention outputs, six rotating buffer sets",
                    "rows": rows, "cols": cols, "buffer_sets": P, "parallelism": "single GPU"},
-        "kernels_us": {"mxfp8_e4m3_quantize": round(ms * 1e3, 3),
+        "kernels_us": {"mxfp8_e4m3_quantize": us_stats(st),
+                       "timing": f"median of {WINDOWS} windows of {args.steps} launches",
                        "mxfp8_e4m3_quantize_128x2048_graph": round(decode_us, 3)},
         "roofline": {"bound": "hbm", "kernel": "mxfp8_e4m3_quantize",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": read_counters(MX_COUNTERS_FILE, MX_SOURCES, "mxfp8.hip"),
                      "algorithmic_bytes_per_launch": algo},
+        "machine": machine_info(torch, clk),
     }
     if not args.no_cpu:
         import oracle
@@ -574,7 +595,9 @@ def bench_dequant(args):
         calls[i % P]()
     torch.cuda.synchronize()
     K = args.steps
-    ms = timed(torch, stream, lambda i: calls[i % P](), K)
+    clk = []
+    st = windowed(torch, stream, lambda i: calls[i % P](), K, clk)
+    ms = st["median"]
     algo = total * (9216 + 4 + 16384) + R * 8
     achieved = algo / (ms * 1e-3) / 1e9
     result = {
@@ -585,12 +608,14 @@ def bench_dequant(args):
         "config": {"workload": "gather-dequantize of the 500K-token decode batch: 4 requests x "
                                "3,906 NVFP4 pages into contiguous E4M3 pages",
                    "pages": total, "index_k_pools": P, "parallelism": "single GPU"},
-        "kernels_us": {"nvfp4_index_k_dequant": round(ms * 1e3, 3)},
+        "kernels_us": {"nvfp4_index_k_dequant": us_stats(st),
+                       "timing": f"median of {WINDOWS} windows of {K} launches"},
         "roofline": {"bound": "hbm", "kernel": "nvfp4_index_k_dequant",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": read_counters(DQ_COUNTERS_FILE, DQ_SOURCES, "dequant.hip"),
                      "algorithmic_bytes_per_launch": algo},
+        "machine": machine_info(torch, clk),
     }
     if not args.no_cpu:
         import numpy as np
@@ -716,9 +741,15 @@ def stats(values):
             "spread": (v[-1] - v[0]) / med if med > 0 else None}
 
 
-def windows(torch, stream, fn, n, count=WINDOWS):
-    """`count` windows of `n` back-to-back calls: ms per call of each."""
-    return [timed(torch, stream, fn, n) for _ in range(count)]
+def windowed(torch, stream, fn, n, clk):
+    """Statistics (ms per call) of WINDOWS windows of `n` back-to-back calls,
+    reading the shader clock into `clk` while each window runs."""
+    return stats([timed_sampling_clock(torch, stream, fn, n, clk) for _ in range(WINDOWS)])
+
+
+def us_stats(st):
+    """A stats() dict in microseconds (the spread stays a fraction)."""
+    return {k: (round(v * 1e3, 3) if k != "spread" else round(v, 4)) for k, v in st.items()}
 
 
 def _capture(torch, dev, make_step, steps):
@@ -1010,8 +1041,7 @@ def bench_decode(args, leg, cpu_legs):
     achieved = algo_bytes / (score_ms["median"] * 1e-3) / 1e9
     traffic = read_counters(counters_file(leg))
 
-    def us(st):
-        return {k: (round(v * 1e3, 3) if k != "spread" else round(v, 4)) for k, v in st.items()}
+    us = us_stats
 
     result = {
         "metric": METRIC if leg == "decode" else
