@@ -187,7 +187,8 @@ def bench_prefill(args):
         "timing": {"windows": WINDOWS, "step_us": us_stats(step_st)},
         "kernels_us": {"indexer_score_prefill": us_stats(score_st),
                        "topk16_select": us_stats(topk_st),
-                       "timing": f"each kernel alone, median of {WINDOWS} windows of {K} launches"},
+                       "timing": f"each kernel alone, median of {WINDOWS} windows of {K} launches",
+                       "indexer_score_prefill_sustained": sustained_calls(torch, dev, [score_call])},
         "roofline": {"bound": "mfma", "kernel": "indexer_score_prefill",
                      "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
@@ -279,7 +280,9 @@ def bench_ragged_prefill(args):
         "timing": {"windows": WINDOWS, "step_us": us_stats(step_st)},
         "kernels_us": {"indexer_score_prefill_ragged": us_stats(score_st),
                        "topk16_select": us_stats(topk_st),
-                       "timing": f"each kernel alone, median of {WINDOWS} windows of {K} launches"},
+                       "timing": f"each kernel alone, median of {WINDOWS} windows of {K} launches",
+                       "indexer_score_prefill_ragged_sustained": sustained_calls(torch, dev,
+                                                                                 [score_call])},
         "roofline": {"bound": "mfma", "kernel": "indexer_score_prefill_ragged",
                      "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
@@ -390,7 +393,8 @@ def bench_nvfp4_prefill(args):
         "kernels_us": {"nvfp4_index_k_dequant": us_stats(gather_st),
                        "indexer_score_prefill": us_stats(score_st),
                        "topk16_select": us_stats(topk_st),
-                       "timing": f"each kernel alone, median of {WINDOWS} windows of {K} launches"},
+                       "timing": f"each kernel alone, median of {WINDOWS} windows of {K} launches",
+                       "indexer_score_prefill_sustained": sustained_calls(torch, dev, [score_call])},
         "roofline": {"bound": "hbm", "kernel": "indexer_score_prefill",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
@@ -528,6 +532,7 @@ def bench_mxfp8(args):
                    "rows": rows, "cols": cols, "buffer_sets": P, "parallelism": "single GPU"},
         "kernels_us": {"mxfp8_e4m3_quantize": us_stats(st),
                        "timing": f"median of {WINDOWS} windows of {args.steps} launches",
+                       "mxfp8_e4m3_quantize_sustained": sustained_calls(torch, dev, calls),
                        "mxfp8_e4m3_quantize_128x2048_graph": round(decode_us, 3)},
         "roofline": {"bound": "hbm", "kernel": "mxfp8_e4m3_quantize",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -609,7 +614,8 @@ def bench_dequant(args):
                                "3,906 NVFP4 pages into contiguous E4M3 pages",
                    "pages": total, "index_k_pools": P, "parallelism": "single GPU"},
         "kernels_us": {"nvfp4_index_k_dequant": us_stats(st),
-                       "timing": f"median of {WINDOWS} windows of {K} launches"},
+                       "timing": f"median of {WINDOWS} windows of {K} launches",
+                       "nvfp4_index_k_dequant_sustained": sustained_calls(torch, dev, calls)},
         "roofline": {"bound": "hbm", "kernel": "nvfp4_index_k_dequant",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -860,6 +866,14 @@ def sustained_power(torch, dev, make_step, seconds=1.0, steps=GRAPH_STEPS):
             "power_cap_w": round(cap / 1e6, 1) if cap else None,
             "us_per_step": round(a.elapsed_time(b) * 1e3 / (n * steps), 3),
             "seconds": round(a.elapsed_time(b) / 1e3, 3), "samples": len(got)}
+
+
+def sustained_calls(torch, dev, calls):
+    """sustained_power() of prepared calls taken in turn, one per step."""
+    def make():
+        cs = [c.again() for c in calls]
+        return lambda i: cs[i % len(cs)]()
+    return sustained_power(torch, dev, make)
 
 
 def machine_info(torch, sclk_samples):

@@ -264,6 +264,12 @@ class PreparedCall:
         if code != 0:
             raise PageScoreError(self._name, code)
 
+    def again(self) -> "PreparedCall":
+        """The same call prepared afresh on the stream that is current now
+        (to capture it into a graph on another stream)."""
+        args, kwargs = self._keep
+        return prepare(globals()[self._name], *args, **kwargs)
+
 
 def _capture_args(fn, *a, **kw):
     """Run `fn` with the C function swapped for a recorder, returning its argument list."""
