@@ -80,3 +80,32 @@ def test_ragged_prefill_and_mxfp8_in_a_graph():
 
     announce("graph: ragged prefill, top-16, mxfp8")
     _replay_check(chain, [scores, row_len, out, xq, xs])
+
+
+def test_prepared_calls_eager_and_in_a_graph():
+    """PreparedCall launches exactly what the direct call launches, and
+    again() re-marshals it on the stream current at that time, so it can be
+    captured into a graph on a side stream."""
+    import page_scoring_top_amd as ps
+    d = workloads.tiny_decode()
+    W = d.width
+    kv, bt, seq = dev(d.kv_cache), dev(d.block_table), dev(d.seq_lens)
+    q, qs = dev(d.q), dev(d.q_scale)
+    direct = torch.zeros((1, 32, W), device="cuda")
+    own_d = torch.zeros((1, 32), dtype=torch.int32, device="cuda")
+    ps.indexer_score_decode(kv, bt, seq, q, qs, d.qlen, W, direct, own_d)
+    torch.cuda.synchronize()
+
+    scores = torch.zeros((1, 32, W), device="cuda")
+    own = torch.zeros((1, 32), dtype=torch.int32, device="cuda")
+    call = ps.prepare(ps.indexer_score_decode, kv, bt, seq, q, qs, d.qlen, W, scores, own)
+    announce("prepared call: tiny decode, eager")
+    call()
+    torch.cuda.synchronize()
+    assert torch.equal(scores, direct) and torch.equal(own, own_d)
+
+    announce("prepared call: tiny decode, again() captured on a side stream")
+    scores.zero_()
+    own.zero_()
+    _replay_check(lambda: call.again()(), [scores, own])
+    assert torch.equal(scores, direct) and torch.equal(own, own_d)
