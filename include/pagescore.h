@@ -227,6 +227,42 @@ int topk16_select(const float *scores, int64_t row_stride, int32_t num_rows,
                   void *stream);
 
 /*
+ * indexer_prefill_topk16 -- the top-16 key ids of every prefill query row
+ * without the score matrix: out[t] is exactly what topk16_select (valid_len,
+ * force and append ranges NULL, width N) writes for row t of the scores
+ * indexer_score_prefill computes from the same arguments ([MOJO] module
+ * description for the scores, which feed a top-k; [MSA] for the order).
+ *
+ * The scores are computed twice in part, never stored: a first pass keeps
+ * only each token's block maxima (a block is 32 keys: 1024 j + c + 32 i,
+ * i < 32, for block 32 j + c) in the workspace; topk16_select picks the 16
+ * best blocks of every token; a last pass recomputes, with the identical
+ * arithmetic, the keys of the blocks whose maximum reaches the 16th of them
+ * (no key outside them can be among the best 16) and selects the exact
+ * top-16.  Ties in the score make more blocks qualify and cost time, not
+ * exactness.
+ *
+ *   q, q_scale, k, k_scale, T, H, N  as for indexer_score_prefill, with
+ *             1 <= H <= PAGESCORE_PREFILL_TOPK_MAX_HEADS and N >= 1.
+ *   out       [T, out_stride] int32, out_stride >= 16; the first 16 entries
+ *             of every row are written (-1 past the N-th when N < 16).
+ *   workspace device memory of at least
+ *             indexer_prefill_topk16_workspace(T, N) bytes, 256-byte
+ *             aligned, owned by the caller; its contents on entry do not
+ *             matter and on return are unspecified.  Calls sharing a
+ *             workspace must be ordered (the same stream).
+ * T == 0 returns PAGESCORE_OK with no launch.  PAGESCORE_EINVAL for H or N
+ * out of range, a null or misaligned pointer, a short out_stride, or a
+ * workspace smaller than required.
+ */
+#define PAGESCORE_PREFILL_TOPK_MAX_HEADS 64
+int64_t indexer_prefill_topk16_workspace(int32_t T, int32_t N);
+int indexer_prefill_topk16(const uint8_t *q, const float *q_scale, const uint8_t *k,
+                           const float *k_scale, int32_t T, int32_t H, int32_t N, int32_t *out,
+                           int64_t out_stride, void *workspace, int64_t workspace_bytes,
+                           void *stream);
+
+/*
  * mxfp8_e4m3_quantize -- MXFP8 quantization of bf16 rows, the step after the
  * sparse attention ([ROCM] "How it works": output layout and arithmetic).
  * Each block of 32 consecutive elements of a row gets one E8M0 scale byte

@@ -32,8 +32,12 @@ _lib.topk16_select.argtypes = [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _I64, _
 _lib.mxfp8_e4m3_quantize.argtypes = [_P, _I64, _I32, _I32, _P, _I64, _P, _I64, _P]
 _lib.indexer_score_prefill_ragged.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P,
                                               _I32, _I32, _P, _I64, _P, _P]
+_lib.indexer_prefill_topk16.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _P, _I64, _P, _I64, _P]
+_lib.indexer_prefill_topk16_workspace.argtypes = [_I32, _I32]
+_lib.indexer_prefill_topk16_workspace.restype = ctypes.c_int64
 for _f in (_lib.nvfp4_index_k_dequant, _lib.indexer_score_decode, _lib.indexer_score_prefill,
-           _lib.topk16_select, _lib.mxfp8_e4m3_quantize, _lib.indexer_score_prefill_ragged):
+           _lib.topk16_select, _lib.mxfp8_e4m3_quantize, _lib.indexer_score_prefill_ragged,
+           _lib.indexer_prefill_topk16):
     _f.restype = ctypes.c_int
 _lib.pagescore_strerror.argtypes = [ctypes.c_int]
 _lib.pagescore_strerror.restype = ctypes.c_char_p
@@ -222,6 +226,44 @@ def topk16_select(scores, width: int, out, valid_len=None, force_begin=None, for
         _ptr(scores), scores.stride(0), int(num_rows), int(width), _ptr(valid_len),
         _ptr(force_begin), _ptr(force_end), _ptr(append_page), _ptr(out), out.stride(0),
         _stream(scores)))
+    return out
+
+
+def prefill_topk16_workspace_bytes(T: int, N: int) -> int:
+    """Bytes of workspace indexer_prefill_topk16 needs for T query rows and N keys."""
+    n = int(_lib.indexer_prefill_topk16_workspace(int(T), int(N)))
+    if n < 0:
+        raise ValueError("T >= 0 and N >= 1 expected")
+    return n
+
+
+def prefill_topk16_workspace(T: int, N: int, device):
+    """A uint8 device tensor big enough to serve as that workspace."""
+    return torch.empty(prefill_topk16_workspace_bytes(T, N), dtype=torch.uint8, device=device)
+
+
+def indexer_prefill_topk16(q, q_scale, k, k_scale, out, workspace):
+    """Top-16 key ids of every row of the lightning-indexer scores of ``q [T,H,128]``
+    against ``k [N,128]`` into ``out [T, >=16]``, without the score matrix
+    (``workspace``: a uint8 device tensor from ``prefill_topk16_workspace``)."""
+    _need(q, "q", _U8)
+    _need(q_scale, "q_scale", _F32)
+    _need(k, "k", _U8)
+    _need(k_scale, "k_scale", _F32)
+    _need(out, "out", _I32T)
+    _need(workspace, "workspace", (torch.uint8,))
+    T, H = q.shape[0], q.shape[1]
+    N = k.shape[0]
+    if not all(t.is_contiguous() for t in (q, q_scale, k, k_scale, workspace)):
+        raise ValueError("q, q_scale, k, k_scale and workspace must be contiguous")
+    if q.dim() != 3 or q.shape[2] != 128 or k.dim() != 2 or k.shape[1] != 128 or \
+            q_scale.numel() < T * H or k_scale.numel() < N:
+        raise ValueError("q [T,H,128], q_scale [T,H], k [N,128], k_scale [N] expected")
+    if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] < T or out.shape[1] < 16:
+        raise ValueError("out must be [T, >=16] with unit column stride")
+    _check("indexer_prefill_topk16", _lib.indexer_prefill_topk16(
+        _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), T, H, N, _ptr(out), out.stride(0),
+        _ptr(workspace), workspace.numel(), _stream(q)))
     return out
 
 

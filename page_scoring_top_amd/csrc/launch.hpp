@@ -44,6 +44,14 @@ hipError_t launch_score_prefill_ragged(const uint8_t *q, const float *q_scale, c
                                        int32_t width, float *scores, int64_t ld, int32_t *row_len,
                                        int num_cus, hipStream_t stream);
 
+// Block columns per token of the fused prefill top-16 (32 per 1,024 keys).
+int64_t prefill_topk16_blocks(int32_t N);
+
+hipError_t launch_prefill_topk16(const uint8_t *q, const float *q_scale, const uint8_t *k,
+                                 const float *k_scale, int32_t T, int32_t H, int32_t N, int32_t *out,
+                                 int64_t out_stride, float *bmax, int32_t *best_blocks, int num_cus,
+                                 hipStream_t stream);
+
 hipError_t launch_topk16(const float *scores, int64_t row_stride, int32_t num_rows, int32_t width,
                          const int32_t *valid_len, const int32_t *force_begin,
                          const int32_t *force_end, const int32_t *append_page, int32_t *out,

@@ -31,6 +31,7 @@
 // token of the group against them.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "wave_keys.hpp"
 
 namespace pagescore {
 
@@ -182,6 +183,13 @@ constexpr int kPackHeads = 4;                                 // heads per token
 // at 2,048 tokens x 65,536 keys.
 constexpr int kStreamingStore = 2;
 constexpr int64_t kPackMaxLd = 1 << 24;                       // 16 rows of scores <= 2^30 bytes
+// Block-maximum mode (the first pass of the fused top-16): a block is one
+// lane's column of 32 consecutive key tiles, i.e. the 32 keys
+// 1024 j + c + 32 i (i = 0..31) of block 32 j + c, so a row of N keys has
+// 32 ceil(N / 1024) blocks and a lane keeps its block's running maximum in
+// one register.
+constexpr int kBlockTiles = 32;
+constexpr int kBlockKeys = kBlockTiles * kKeysPerTile;        // 1,024
 
 
 // kPack: up to four heads, a wave takes 8 kHT tokens and row 4 u + h of its
@@ -205,7 +213,11 @@ typedef float KeyScales[kChunkBufs][kChunkKeys];
 // (ke clamped to the row width); first_split: the unit holding column 0
 // writes row_len.  kbuf / ks_lds: the work-group's LDS key chunks.  Every
 // thread of the work-group calls it with the same arguments.
-template <int kHT, bool kPack, bool kCausal>
+// kBlockMax (dense only): instead of the scores, `scores` receives each
+// block's maximum score (rows of `ld` blocks; NaN scores are ignored, as the
+// key order ranks NaN lowest), and keys past the range count as NaN.  The
+// work-group's first key kb must then be a multiple of kBlockKeys.
+template <int kHT, bool kPack, bool kCausal, bool kBlockMax = false>
 __device__ __forceinline__ void prefill_unit(
     KeyChunks &kbuf, KeyScales &ks_lds, const uint8_t *__restrict__ q,
     const float *__restrict__ q_scale, const uint8_t *__restrict__ k,
@@ -317,6 +329,8 @@ __device__ __forceinline__ void prefill_unit(
         for (int i = 0; i < 2; ++i)
             r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, ck * kDepth + cd + 16 * i, 0, 0);
         r.ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, 4 * ck, 0, 0));
+        if constexpr (kBlockMax)
+            r.ks = ck < live ? r.ks : __builtin_nanf("");
     };
     // Piece j (0..3) of a chunk's conversion; piece 3 also stores the key
     // scale (the key's four threads store the same value).
@@ -334,9 +348,12 @@ __device__ __forceinline__ void prefill_unit(
     // lane's row of token 8 (g / 4) + 2 (g % 4) + half (kDropped for a token
     // past T), plus the key's offset (plus kKeyDropped for a key past ke):
     // every dropped offset lies past the records, and none wraps.
+    // Block-maximum mode: the work-group's blocks start at column kb / 32.
+    const int out_col0 = kBlockMax ? kb / kBlockKeys * kKeysPerTile : kb;
+    const int out_cols = kBlockMax ? (ke - kb + kBlockKeys - 1) / kBlockKeys * kKeysPerTile : ke - kb;
     const __amdgpu_buffer_rsrc_t out = uniform_rsrc(
-        scores + (tok_ok ? t : 0) * ld + kb,
-        tok_ok ? (uint32_t)(((int64_t)(tok_rows - 1) * ld + (ke - kb)) * 4) : 0u);
+        scores + (tok_ok ? t : 0) * ld + out_col0,
+        tok_ok ? (uint32_t)(((int64_t)(tok_rows - 1) * ld + out_cols) * 4) : 0u);
     const int key_count = ke - kb;
     uint32_t row_off[kPack ? 4 * kHT : 1];
     // Causal: a store of column kb + n writes -inf unless n < vis_rel (the
@@ -365,6 +382,12 @@ __device__ __forceinline__ void prefill_unit(
     v16f acc[2][kHT];
     float y[4];
     float part[kParts];
+    // Block-maximum mode: running maxima of the lane's current block, one
+    // per score the lane produces per tile.
+    float bmx[kPack ? kParts : 1];
+#pragma unroll
+    for (int g = 0; g < (kPack ? kParts : 1); ++g)
+        bmx[g] = -__builtin_huge_valf();
     auto part_of = [](int e) { return kPack ? e / 4 : e % 4; };
     auto first_of_part = [](int e) { return kPack ? e % 4 == 0 : e < 4; };
     auto add_term = [&](int e) {
@@ -399,6 +422,10 @@ __device__ __forceinline__ void prefill_unit(
 #pragma unroll
             for (int g = 0; g < kParts; ++g) {
                 float v = hks * part[g];
+                if constexpr (kBlockMax) {
+                    bmx[g] = __builtin_fmaxf(bmx[g], v);
+                    continue;
+                }
                 if constexpr (kCausal)
                     v = n < vis_rel[g] ? v : -INFINITY;
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), out, row_off[g] + key_off, 0,
@@ -412,9 +439,29 @@ __device__ __forceinline__ void prefill_unit(
         const float total = sum + __uint_as_float(sw[1]);   // lanes 0..31: the other half's sum
         const uint32_t off = (half == 0 && n_rel >= 0) ? (uint32_t)(n_rel + col) * 4u : kDropped;
         float v = ks * (0.5f * total);
+        if constexpr (kBlockMax) {
+            bmx[0] = __builtin_fmaxf(bmx[0], v);
+            return;
+        }
         if constexpr (kCausal)
             v = n_rel + col < vis_rel[0] ? v : -INFINITY;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), out, off, 0, 0);
+    };
+    // Block-maximum mode: store the maxima of the block holding the tile
+    // whose first key is n_rel, and start the next block.
+    auto flush_blocks = [&](int n_rel) {
+        const uint32_t boff = (uint32_t)(n_rel / kBlockKeys * kKeysPerTile + col) * 4u;
+        if constexpr (kPack) {
+#pragma unroll
+            for (int g = 0; g < kParts; ++g) {
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bmx[g]), out, row_off[g] + boff, 0, 0);
+                bmx[g] = -__builtin_huge_valf();
+            }
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bmx[0]), out,
+                                                  half == 0 ? boff : kDropped, 0, 0);
+            bmx[0] = -__builtin_huge_valf();
+        }
     };
 
     // B operand of tile kt, K step st of the chunk in buffer buf.
@@ -488,7 +535,17 @@ __device__ __forceinline__ void prefill_unit(
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            drain_tail(ks_prev, n_prev);
+            if constexpr (kBlockMax) {
+                // The drain before the first tile has no scores; a block
+                // ends with its 32nd tile.
+                if (n_prev >= 0) {
+                    drain_tail(ks_prev, n_prev);
+                    if ((n_prev / kKeysPerTile) % kBlockTiles == kBlockTiles - 1)
+                        flush_blocks(n_prev);
+                }
+            } else {
+                drain_tail(ks_prev, n_prev);
+            }
             ks_prev = ks;
             n_prev = c * kChunkKeys + kt * kKeysPerTile;
             __builtin_amdgcn_sched_barrier(0);
@@ -500,7 +557,15 @@ __device__ __forceinline__ void prefill_unit(
 #pragma unroll
     for (int m = 0; m < 8 * kHT; ++m)
         drain_slice(acc[(kTilesPerChunk - 1) & 1], m);
-    drain_tail(ks_prev, n_prev);
+    if constexpr (kBlockMax) {
+        // The last tile's block (complete or not).
+        if (n_prev >= 0) {
+            drain_tail(ks_prev, n_prev);
+            flush_blocks(n_prev);
+        }
+    } else {
+        drain_tail(ks_prev, n_prev);
+    }
     if constexpr (kCausal) {
         // The -inf tail past the computed chunks: columns [kb + 128 chunks, ke)
         // of the wave's rows.
@@ -514,7 +579,7 @@ __device__ __forceinline__ void prefill_unit(
 }
 
 // One unit per work-group: grid (token groups, key splits, sequences).
-template <int kHT, bool kPack, bool kCausal>
+template <int kHT, bool kPack, bool kCausal, bool kBlockMax = false>
 __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel(
     const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
     const uint8_t *__restrict__ k, const float *__restrict__ k_scale, int32_t T, int32_t H,
@@ -524,9 +589,9 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
     __shared__ KeyScales ks_lds;
     constexpr int kTokPerGroup = kH64Waves * (kPack ? 8 * kHT : 1);
     const int kb = blockIdx.y * keys_per_group;
-    prefill_unit<kHT, kPack, kCausal>(kbuf, ks_lds, q, q_scale, k, k_scale, T, H, N, scores, ld, rb,
-                                      blockIdx.z, blockIdx.x * kTokPerGroup, kb,
-                                      (int64_t)kb + keys_per_group, blockIdx.y == 0);
+    prefill_unit<kHT, kPack, kCausal, kBlockMax>(kbuf, ks_lds, q, q_scale, k, k_scale, T, H, N, scores,
+                                                 ld, rb, blockIdx.z, blockIdx.x * kTokPerGroup, kb,
+                                                 (int64_t)kb + keys_per_group, blockIdx.y == 0);
 }
 
 // Chunks a causal query group computes: its last query's visible keys
@@ -631,6 +696,223 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_balanced_k
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fused top-16 of prefill score rows (indexer_prefill_topk16), without the
+// score matrix.  Three passes:
+//  1. the score kernel in block-maximum mode writes each token's block
+//     maxima (kBlockKeys);
+//  2. topk16_select picks each token's 16 best blocks; the 16th of their
+//     maxima, B16, bounds the token's 16th best score from below, since the
+//     16 blocks hold 16 distinct keys scoring at least B16;
+//  3. this kernel rescores, with the score kernel's arithmetic, the blocks
+//     whose maximum reaches B16 (no other block holds a key scoring B16 or
+//     more), keeps the keys scoring at least B16 (among them the best 16),
+//     and sorts those by the full key order.
+// Rescoring gives the very bits the score kernel computes: the same f16
+// operands in the same MFMA (each accumulator element depends only on its
+// own row and column), eight K steps in the same order, and the same
+// epilogue operations in the same order.
+// ---------------------------------------------------------------------------
+constexpr int kRescoreWaves = 4;
+constexpr int kSurvCap = 256;    // survivors a token holds before compacting to its best 16
+constexpr int kCandBatch = 4;    // candidate blocks whose keys are loaded together
+
+// Wave maximum of a 64-bit value (butterfly over the lane distances).
+template <int J>
+__device__ __forceinline__ uint64_t max_with_lane_xor(uint64_t x, int lane)
+{
+    const uint32_t lo = xor_lane<J>((uint32_t)x, lane);
+    const uint32_t hi = xor_lane<J>((uint32_t)(x >> 32), lane);
+    const uint64_t y = ((uint64_t)hi << 32) | lo;
+    return y > x ? y : x;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x, int lane)
+{
+    x = max_with_lane_xor<1>(x, lane);
+    x = max_with_lane_xor<2>(x, lane);
+    x = max_with_lane_xor<4>(x, lane);
+    x = max_with_lane_xor<8>(x, lane);
+    x = max_with_lane_xor<16>(x, lane);
+    return max_with_lane_xor<32>(x, lane);
+}
+
+// The best 16 of the first `count` (at most kSurvCap) keys of a wave's LDS
+// list, descending in lanes 0..15 (0 where there are fewer).  Up to 64 keys:
+// one bitonic sort; more: sixteen rounds of taking the wave's largest key.
+__device__ __forceinline__ uint64_t best16_of_list(const uint64_t *list, int count, int lane)
+{
+    if (count <= kWave)
+        return wave_sort_desc<kWave>(lane < count ? list[lane] : 0ull, lane);
+    constexpr int kPer = kSurvCap / kWave;
+    uint64_t v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+        v[j] = lane + kWave * j < count ? list[lane + kWave * j] : 0ull;
+    uint64_t res = 0;
+    for (int r = 0; r < kTopk; ++r) {
+        uint64_t m = v[0];
+#pragma unroll
+        for (int j = 1; j < kPer; ++j)
+            m = v[j] > m ? v[j] : m;
+        m = wave_max_u64(m, lane);
+        res = lane == r ? m : res;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            v[j] = v[j] == m ? 0ull : v[j];   // keys are distinct: one lane drops it
+    }
+    return res;
+}
+
+// One token per wave.  kHT, kPack: the score kernel's variant (packed, the
+// token sits in rows 0..3 of a one-tile group; otherwise kHT 32-head tiles).
+template <int kHT, bool kPack>
+__global__ __launch_bounds__(kRescoreWaves * kWave) void prefill_topk_rescore_kernel(
+    const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
+    const uint8_t *__restrict__ k, const float *__restrict__ k_scale, int32_t T, int32_t H,
+    int32_t N, const float *__restrict__ bmax, int32_t nblocks,
+    const int32_t *__restrict__ best_blocks, int32_t *__restrict__ out, int64_t out_stride)
+{
+    __shared__ uint64_t surv[kRescoreWaves][kSurvCap];
+    __shared__ int32_t cand[kRescoreWaves][kWave];
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    const int64_t t = (int64_t)blockIdx.x * kRescoreWaves + wave;
+    if (t >= T)
+        return;   // no work-group barrier follows
+    uint64_t *list = surv[wave];
+    int32_t *cl = cand[wave];
+
+    constexpr int kTiles = kPack ? 1 : kHT;
+    u32x4 a[kTiles][8];
+    float qs[kTiles][16];
+#pragma unroll
+    for (int ht = 0; ht < kTiles; ++ht) {
+        const int h = kPack ? col % 4 : 32 * ht + col;
+        const bool ok = (!kPack || col < 4) && h < H;
+        const uint8_t *src = q + (t * H + (ok ? h : 0)) * kDepth + 8 * half;
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            uint2 b = make_uint2(0u, 0u);
+            if (ok)
+                b = *reinterpret_cast<const uint2 *>(src + 16 * st);
+            a[ht][st] = f16_of_8_bytes(b.x, b.y);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int hh = kPack ? i % 4 : 32 * ht + 8 * (i / 4) + 4 * half + i % 4;
+            const bool mine = !kPack || (i < 4 && half == 0);
+            qs[ht][i] = (mine && hh < H) ? q_scale[t * H + hh] : 0.0f;
+        }
+    }
+    // The score of key `n` of lane col (lanes 0..31): the score kernel's
+    // epilogue, term for term.
+    auto score_of = [&](const uint2 (&kr)[8], float ks) {
+        v16f acc[kTiles];
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            const u32x4 bop = f16_of_8_bytes(kr[st].x, kr[st].y);
+#pragma unroll
+            for (int ht = 0; ht < kTiles; ++ht)
+                acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a[ht][st]),
+                                                                 __builtin_bit_cast(v8h, bop),
+                                                                 st == 0 ? v16f{} : acc[ht], 0, 0, 0);
+        }
+        if constexpr (kPack) {
+            float part = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x = acc[0][e];
+                const float y = x + fabsf(x);
+                part = e == 0 ? y * qs[0][e] : fmaf(y, qs[0][e], part);
+            }
+            const float hks = 0.5f * ks;
+            return hks * part;
+        } else {
+            float part[4];
+#pragma unroll
+            for (int e = 0; e < 16 * kTiles; ++e) {
+                const float x = acc[e / 16][e % 16];
+                const float y = x + fabsf(x);
+                part[e % 4] = e < 4 ? y * qs[e / 16][e % 16] : fmaf(y, qs[e / 16][e % 16], part[e % 4]);
+            }
+            const float sum = (part[0] + part[1]) + (part[2] + part[3]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum),
+                                                             false, false);
+            const float total = sum + __uint_as_float(sw[1]);
+            return ks * (0.5f * total);
+        }
+    };
+
+    // B16 (the best blocks come from topk16_select: 16 valid ids, since a
+    // row has at least 32 blocks).
+    const int32_t b16 = best_blocks[t * kTopk + kTopk - 1];
+    const float *brow = bmax + t * nblocks;
+    uint32_t thr = key_hi(b16 >= 0 && b16 < nblocks ? brow[b16] : -__builtin_huge_valf(), false);
+    int count = 0;
+    for (int base = 0; base < nblocks; base += kWave) {
+        const int b = base + lane;
+        const bool is_cand = b < nblocks && key_hi(brow[b], false) >= thr;
+        const uint64_t mask = __ballot(is_cand);
+        if (is_cand)
+            cl[__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u))] = b;
+        const int nc = lanes_set(mask);
+        wave_lds_sync();
+        for (int j0 = 0; j0 < nc; j0 += kCandBatch) {
+            uint2 kr[kCandBatch][8];
+            float ksv[kCandBatch];
+            int64_t nk[kCandBatch];
+#pragma unroll
+            for (int cb = 0; cb < kCandBatch; ++cb) {
+                const int blk = j0 + cb < nc ? cl[j0 + cb] : -1;
+                const int64_t n = blk >= 0 ? (int64_t)(blk / kKeysPerTile) * kBlockKeys + blk % kKeysPerTile +
+                                                 (int64_t)kKeysPerTile * col
+                                           : (int64_t)N;
+                const bool live = n < N;
+                nk[cb] = n;
+                const uint2 *src = reinterpret_cast<const uint2 *>(k + (live ? n : 0) * kDepth + 8 * half);
+#pragma unroll
+                for (int st = 0; st < 8; ++st)
+                    kr[cb][st] = live ? src[2 * st] : make_uint2(0u, 0u);
+                ksv[cb] = live ? k_scale[n] : __builtin_nanf("");
+            }
+#pragma unroll
+            for (int cb = 0; cb < kCandBatch; ++cb) {
+                if (j0 + cb >= nc)
+                    break;
+                const float v = score_of(kr[cb], ksv[cb]);
+                const uint32_t hi = key_hi(v, false);
+                const bool keep = half == 0 && nk[cb] < N && hi >= thr;
+                const uint64_t km = __ballot(keep);
+                const int nkeep = lanes_set(km);
+                if (count + nkeep > kSurvCap) {
+                    // Compact to the best 16 and raise the bar to the 16th.
+                    wave_lds_sync();
+                    const uint64_t best = best16_of_list(list, count, lane);
+                    wave_lds_sync();
+                    if (lane < kTopk)
+                        list[lane] = best;
+                    const uint32_t hi16 = __builtin_amdgcn_readlane((uint32_t)(best >> 32), kTopk - 1);
+                    thr = hi16 > thr ? hi16 : thr;
+                    count = kTopk;
+                    wave_lds_sync();
+                }
+                if (keep)
+                    list[count + __builtin_amdgcn_mbcnt_hi((uint32_t)(km >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)km, 0u))] =
+                        make_key(hi, (int)nk[cb]);
+                count += nkeep;
+            }
+        }
+        wave_lds_sync();   // before the next window's ids overwrite cl
+    }
+    const uint64_t best = best16_of_list(list, count, lane);
+    if (lane < kTopk)
+        out[t * out_stride + lane] = best != 0 ? key_col(best) : -1;
+}
+
 }  // namespace
 
 static_assert(kPrefillMaxHeads * ((kRowHalves * 2) + 4) <= kLdsBytes,
@@ -724,6 +1006,74 @@ hipError_t launch_score_prefill_ragged(const uint8_t *q, const float *q_scale, c
     }
     return launch_h64<true>(q, q_scale, k, k_scale, T, H, N, scores, ld, max_q, width, num_seqs, rb,
                             stream);
+}
+
+int64_t prefill_topk16_blocks(int32_t N)
+{
+    return ((int64_t)N + kBlockKeys - 1) / kBlockKeys * kKeysPerTile;
+}
+
+hipError_t launch_prefill_topk16(const uint8_t *q, const float *q_scale, const uint8_t *k,
+                                 const float *k_scale, int32_t T, int32_t H, int32_t N, int32_t *out,
+                                 int64_t out_stride, float *bmax, int32_t *best_blocks, int num_cus,
+                                 hipStream_t stream)
+{
+    if (H > kSmallHeads || T < 1 || N < 1)
+        return hipErrorInvalidValue;
+    const int64_t nblocks = prefill_topk16_blocks(N);
+    if (nblocks > kTopkMaxWidth)
+        return hipErrorInvalidValue;
+    // Pass 1: block maxima, with the score kernel's launch shape (about one
+    // work-group per compute unit), key splits in whole blocks of 1,024.
+    const bool pack = H <= kPackHeads && nblocks <= kPackMaxLd;
+    const int pack_tiles = T > 8 * kH64Waves ? 2 : 1;
+    const int64_t tokens_per_group = (int64_t)kH64Waves * (pack ? 8 * pack_tiles : 1);
+    const int64_t groups = ((int64_t)T + tokens_per_group - 1) / tokens_per_group;
+    if (groups > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    const int64_t block_groups = nblocks / kKeysPerTile;
+    int64_t splits = (256 + groups - 1) / groups;
+    const int64_t min_splits = ((int64_t)N + kMaxKeysPerGroup - 1) / kMaxKeysPerGroup;
+    splits = splits < min_splits ? min_splits : splits;
+    splits = splits < 1 ? 1 : (splits > block_groups ? block_groups : splits);
+    const int64_t keys_per_group = ((block_groups + splits - 1) / splits) * kBlockKeys;
+    splits = ((int64_t)N + keys_per_group - 1) / keys_per_group;
+    if (splits > 65535)
+        return hipErrorInvalidValue;
+    const dim3 grid((uint32_t)groups, (uint32_t)splits, 1u), block(kH64Waves * kWave);
+    const RaggedBatch none{};
+    if (pack && pack_tiles == 2)
+        hipLaunchKernelGGL((score_prefill_h64_kernel<2, true, false, true>), grid, block, 0, stream, q,
+                           q_scale, k, k_scale, T, H, N, (int32_t)keys_per_group, bmax, nblocks, none);
+    else if (pack)
+        hipLaunchKernelGGL((score_prefill_h64_kernel<1, true, false, true>), grid, block, 0, stream, q,
+                           q_scale, k, k_scale, T, H, N, (int32_t)keys_per_group, bmax, nblocks, none);
+    else if (H <= 32)
+        hipLaunchKernelGGL((score_prefill_h64_kernel<1, false, false, true>), grid, block, 0, stream, q,
+                           q_scale, k, k_scale, T, H, N, (int32_t)keys_per_group, bmax, nblocks, none);
+    else
+        hipLaunchKernelGGL((score_prefill_h64_kernel<2, false, false, true>), grid, block, 0, stream, q,
+                           q_scale, k, k_scale, T, H, N, (int32_t)keys_per_group, bmax, nblocks, none);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    // Pass 2: the 16 best blocks of every token.
+    e = launch_topk16(bmax, nblocks, T, (int32_t)nblocks, nullptr, nullptr, nullptr, nullptr,
+                      best_blocks, kTopk, num_cus, stream);
+    if (e != hipSuccess)
+        return e;
+    // Pass 3: rescoring and the exact selection.
+    const dim3 g3((uint32_t)(((int64_t)T + kRescoreWaves - 1) / kRescoreWaves)), b3(kRescoreWaves * kWave);
+    if (pack)
+        hipLaunchKernelGGL((prefill_topk_rescore_kernel<1, true>), g3, b3, 0, stream, q, q_scale, k,
+                           k_scale, T, H, N, bmax, (int32_t)nblocks, best_blocks, out, out_stride);
+    else if (H <= 32)
+        hipLaunchKernelGGL((prefill_topk_rescore_kernel<1, false>), g3, b3, 0, stream, q, q_scale, k,
+                           k_scale, T, H, N, bmax, (int32_t)nblocks, best_blocks, out, out_stride);
+    else
+        hipLaunchKernelGGL((prefill_topk_rescore_kernel<2, false>), g3, b3, 0, stream, q, q_scale, k,
+                           k_scale, T, H, N, bmax, (int32_t)nblocks, best_blocks, out, out_stride);
+    return hipGetLastError();
 }
 
 hipError_t launch_score_prefill(const uint8_t *q, const float *q_scale, const uint8_t *k,

@@ -31,7 +31,8 @@ def lib():
 def test_header_declares_every_call():
     fns = declared_functions()
     for name in ("nvfp4_index_k_dequant", "indexer_score_decode", "indexer_score_prefill",
-                 "indexer_score_prefill_ragged", "topk16_select", "mxfp8_e4m3_quantize"):
+                 "indexer_score_prefill_ragged", "topk16_select", "mxfp8_e4m3_quantize",
+                 "indexer_prefill_topk16", "indexer_prefill_topk16_workspace"):
         assert name in fns
 
 
@@ -123,6 +124,54 @@ def test_prefill_host_checks(lib):
     assert _prefill(lib, q=ODD) == EINVAL
     assert _prefill(lib, k=ODD) == EINVAL
     assert _prefill(lib, ks=None) == EINVAL
+
+
+def _workspace(lib, T, N):
+    f = lib.indexer_prefill_topk16_workspace
+    f.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    f.restype = ctypes.c_int64
+    return f(T, N)
+
+
+def test_prefill_topk16_workspace_size(lib):
+    # Block maxima [T, 32 ceil(N / 1024)] float32 padded to 256 bytes, then [T, 16] int32.
+    assert _workspace(lib, 2048, 65536) == 2048 * 2048 * 4 + 2048 * 64
+    assert _workspace(lib, 5, 1) == 768 + 5 * 64
+    assert _workspace(lib, 3, 1025) == 3 * 64 * 4 + 3 * 64
+    assert _workspace(lib, 0, 7) == 0
+    assert _workspace(lib, -1, 7) < 0
+    assert _workspace(lib, 4, 0) < 0
+
+
+WS = P(0x10000)           # 256-byte aligned, never dereferenced on these paths
+
+
+def _prefill_topk(lib, **kw):
+    a = dict(q=FAKE, qs=FAKE, k=FAKE, ks=FAKE, T=4, H=4, N=100, out=FAKE, os=16, ws=WS,
+             wsb=1 << 20)
+    a.update(kw)
+    f = lib.indexer_prefill_topk16
+    f.argtypes = [P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int64, P,
+                  ctypes.c_int64, P]
+    return f(a["q"], a["qs"], a["k"], a["ks"], a["T"], a["H"], a["N"], a["out"], a["os"], a["ws"],
+             a["wsb"], None)
+
+
+def test_prefill_topk16_host_checks(lib):
+    # Every call below fails one check (or has T == 0), so nothing is enqueued.
+    assert _prefill_topk(lib, T=0) == 0
+    assert _prefill_topk(lib, T=-1) == EINVAL
+    assert _prefill_topk(lib, N=0) == EINVAL
+    assert _prefill_topk(lib, H=0) == EINVAL
+    assert _prefill_topk(lib, H=65) == EINVAL
+    assert _prefill_topk(lib, os=15) == EINVAL
+    assert _prefill_topk(lib, q=ODD) == EINVAL
+    assert _prefill_topk(lib, k=ODD) == EINVAL
+    assert _prefill_topk(lib, qs=None) == EINVAL
+    assert _prefill_topk(lib, out=None) == EINVAL
+    assert _prefill_topk(lib, ws=None) == EINVAL
+    assert _prefill_topk(lib, ws=P(0x10010)) == EINVAL          # 16- but not 256-byte aligned
+    assert _prefill_topk(lib, wsb=_workspace(lib, 4, 100) - 1) == EINVAL
 
 
 def _topk(lib, **kw):
