@@ -170,6 +170,7 @@ def bench_prefill(args):
     score_st = windowed(torch, stream, lambda i: score_call(), K, clk)
     topk_st = windowed(torch, stream, lambda i: topk_call(), K, clk)
     ms_per_step, score_ms, topk_ms = step_st["median"], score_st["median"], topk_st["median"]
+    fused = fused_prefill_topk(torch, ps, stream, q, qs, k, ks, out, K, clk, ms_per_step)
     flops = 2.0 * T * N * H * 128          # the contraction (the epilogue is not counted)
     achieved = flops / (score_ms * 1e-3) / 1e12
     result = {
@@ -185,6 +186,8 @@ def bench_prefill(args):
                    "tokens": T, "heads": H, "keys": N, "depth": 128, "parallelism": "single GPU"},
         "top16_rows_per_s": round(T / (topk_ms * 1e-3), 1),
         "timing": {"windows": WINDOWS, "step_us": us_stats(step_st)},
+        "fused_top16": dict(fused, value=round(flops / (fused["step_us"]["median"] * 1e-6) / 1e12, 2),
+                            unit="TFLOP/s"),
         "kernels_us": {"indexer_score_prefill": us_stats(score_st),
                        "topk16_select": us_stats(topk_st),
                        "timing": f"each kernel alone, median of {WINDOWS} windows of {K} launches",
@@ -210,6 +213,30 @@ def bench_prefill(args):
             "sample": f"oracle prefill scores of {n} full rows ({t_rows:.2f} s), scaled to {T} rows; "
                       f"top-16 not included; step estimate {cpu_step:.1f} s"}
     print(json.dumps(result), flush=True)
+
+
+def fused_prefill_topk(torch, ps, stream, q, qs, k, ks, chain_out, K, clk, chain_ms, before=None):
+    """The same step with indexer_prefill_topk16 in place of the score matrix
+    and topk16_select (after `before`, e.g. the gather, when given): its
+    windows, the speed-up over the two-call step, and whether its output
+    equals the two-call step's (run just before)."""
+    T, N = q.shape[0], k.shape[0]
+    ws = ps.prefill_topk16_workspace(T, N, q.device)
+    out = torch.empty_like(chain_out)
+    call = ps.prepare(ps.indexer_prefill_topk16, q, qs, k, ks, out, ws)
+
+    def step(i):
+        if before is not None:
+            before()
+        call()
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out, chain_out))
+    st = windowed(torch, stream, step, K, clk)
+    return {"call": "indexer_prefill_topk16", "step_us": us_stats(st),
+            "speedup_vs_two_call_step": round(chain_ms / st["median"], 3),
+            "matches_two_call_step": same, "workspace_bytes": int(ws.numel())}
 
 
 def bench_ragged_prefill(args):
@@ -374,6 +401,8 @@ def bench_nvfp4_prefill(args):
     score_st = windowed(torch, stream, lambda i: score_call(), K, clk)
     topk_st = windowed(torch, stream, lambda i: topk_call(), K, clk)
     ms_per_step, score_ms = step_st["median"], score_st["median"]
+    fused = fused_prefill_topk(torch, ps, stream, q, qs, keys.view(-1, 128)[:N], ones, out, K, clk,
+                               ms_per_step, before=gather_call)
     # Score kernel: queries, scales and keys read once, every score written once.
     algo = T * H * (128 + 4) + N * (128 + 4) + T * N * 4
     achieved = algo / (score_ms * 1e-3) / 1e9
@@ -390,6 +419,8 @@ def bench_nvfp4_prefill(args):
                                "2,048 tokens x 4 heads x depth 128 scored, top-16 of 2,048 rows",
                    "tokens": T, "heads": H, "keys": N, "pages": P, "parallelism": "single GPU"},
         "timing": {"windows": WINDOWS, "step_us": us_stats(step_st)},
+        "fused_top16": dict(fused, value=round(pairs / (fused["step_us"]["median"] * 1e-6) / 1e9, 3),
+                            unit="G scores/s"),
         "kernels_us": {"nvfp4_index_k_dequant": us_stats(gather_st),
                        "indexer_score_prefill": us_stats(score_st),
                        "topk16_select": us_stats(topk_st),

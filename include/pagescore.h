@@ -233,14 +233,14 @@ int topk16_select(const float *scores, int64_t row_stride, int32_t num_rows,
  * indexer_score_prefill computes from the same arguments ([MOJO] module
  * description for the scores, which feed a top-k; [MSA] for the order).
  *
- * The scores are computed twice in part, never stored: a first pass keeps
- * only each token's block maxima (a block is 32 keys: 1024 j + c + 32 i,
- * i < 32, for block 32 j + c) in the workspace; topk16_select picks the 16
- * best blocks of every token; a last pass recomputes, with the identical
- * arithmetic, the keys of the blocks whose maximum reaches the 16th of them
- * (no key outside them can be among the best 16) and selects the exact
- * top-16.  Ties in the score make more blocks qualify and cost time, not
- * exactness.
+ * The scores are never stored: a first pass keeps, per token and block (a
+ * block is 32 keys: 1024 j + c + 32 i, i < 32, for block 32 j + c), the
+ * largest score, where it occurs and the second largest, in the workspace;
+ * a second pass sets a bar that 16 distinct keys of the row reach (so every
+ * key of the best 16 does), takes the keys at or above it from the records,
+ * recomputing with the identical arithmetic the keys of the rare blocks that
+ * hold two such keys, and selects the exact top-16.  Ties in the score make
+ * more blocks qualify and cost time, not exactness.
  *
  *   q, q_scale, k, k_scale, T, H, N  as for indexer_score_prefill, with
  *             1 <= H <= PAGESCORE_PREFILL_TOPK_MAX_HEADS and N >= 1.

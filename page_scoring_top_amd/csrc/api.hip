@@ -119,23 +119,14 @@ int indexer_score_prefill_ragged(const uint8_t *q, const float *q_scale, const u
         row_len, current_device_cus(), (hipStream_t)stream));
 }
 
-// Workspace of indexer_prefill_topk16: the block maxima [T, blocks] float32,
-// then (at a 256-byte boundary) the best blocks [T, 16] int32; -1 for
-// arguments out of range.
-static int64_t prefill_topk16_layout(int32_t T, int32_t N, int64_t *best_offset)
+// Workspace of indexer_prefill_topk16: the block records, three planes of
+// [T, blocks] (float32 largest and second largest score, int32 tile); -1
+// for arguments out of range.
+int64_t indexer_prefill_topk16_workspace(int32_t T, int32_t N)
 {
     if (T < 0 || N < 1)
         return -1;
-    const int64_t bm_bytes = (int64_t)T * pagescore::prefill_topk16_blocks(N) * 4;
-    const int64_t off = (bm_bytes + 255) / 256 * 256;
-    if (best_offset)
-        *best_offset = off;
-    return off + (int64_t)T * PAGESCORE_TOPK * 4;
-}
-
-int64_t indexer_prefill_topk16_workspace(int32_t T, int32_t N)
-{
-    return prefill_topk16_layout(T, N, nullptr);
+    return (int64_t)T * 3 * pagescore::prefill_topk16_blocks(N) * 4;
 }
 
 int indexer_prefill_topk16(const uint8_t *q, const float *q_scale, const uint8_t *k,
@@ -147,16 +138,13 @@ int indexer_prefill_topk16(const uint8_t *q, const float *q_scale, const uint8_t
         return PAGESCORE_EINVAL;
     if (T == 0)
         return PAGESCORE_OK;
-    int64_t best_off = 0;
-    const int64_t need = prefill_topk16_layout(T, N, &best_off);
     if (!q || !aligned16(q) || !q_scale || !k || !aligned16(k) || !k_scale || !out ||
         out_stride < PAGESCORE_TOPK || !workspace || ((uintptr_t)workspace & 255u) != 0 ||
-        workspace_bytes < need)
+        workspace_bytes < indexer_prefill_topk16_workspace(T, N))
         return PAGESCORE_EINVAL;
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
-    return launch_status(pagescore::launch_prefill_topk16(
-        q, q_scale, k, k_scale, T, H, N, out, out_stride, reinterpret_cast<float *>(ws),
-        reinterpret_cast<int32_t *>(ws + best_off), current_device_cus(), (hipStream_t)stream));
+    return launch_status(pagescore::launch_prefill_topk16(q, q_scale, k, k_scale, T, H, N, out,
+                                                          out_stride, static_cast<float *>(workspace),
+                                                          (hipStream_t)stream));
 }
 
 int topk16_select(const float *scores, int64_t row_stride, int32_t num_rows, int32_t width,

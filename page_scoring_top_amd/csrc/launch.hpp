@@ -49,8 +49,7 @@ int64_t prefill_topk16_blocks(int32_t N);
 
 hipError_t launch_prefill_topk16(const uint8_t *q, const float *q_scale, const uint8_t *k,
                                  const float *k_scale, int32_t T, int32_t H, int32_t N, int32_t *out,
-                                 int64_t out_stride, float *bmax, int32_t *best_blocks, int num_cus,
-                                 hipStream_t stream);
+                                 int64_t out_stride, float *bmax, hipStream_t stream);
 
 hipError_t launch_topk16(const float *scores, int64_t row_stride, int32_t num_rows, int32_t width,
                          const int32_t *valid_len, const int32_t *force_begin,

@@ -186,8 +186,9 @@ constexpr int64_t kPackMaxLd = 1 << 24;                       // 16 rows of scor
 // Block-maximum mode (the first pass of the fused top-16): a block is one
 // lane's column of 32 consecutive key tiles, i.e. the 32 keys
 // 1024 j + c + 32 i (i = 0..31) of block 32 j + c, so a row of N keys has
-// 32 ceil(N / 1024) blocks and a lane keeps its block's running maximum in
-// one register.
+// 32 ceil(N / 1024) blocks and a lane keeps its block's record in three
+// registers: the largest score, the tile i where it first occurs, and the
+// second largest (the largest again on a tie).
 constexpr int kBlockTiles = 32;
 constexpr int kBlockKeys = kBlockTiles * kKeysPerTile;        // 1,024
 
@@ -213,10 +214,12 @@ typedef float KeyScales[kChunkBufs][kChunkKeys];
 // (ke clamped to the row width); first_split: the unit holding column 0
 // writes row_len.  kbuf / ks_lds: the work-group's LDS key chunks.  Every
 // thread of the work-group calls it with the same arguments.
-// kBlockMax (dense only): instead of the scores, `scores` receives each
-// block's maximum score (rows of `ld` blocks; NaN scores are ignored, as the
-// key order ranks NaN lowest), and keys past the range count as NaN.  The
-// work-group's first key kb must then be a multiple of kBlockKeys.
+// kBlockMax (dense only): instead of the scores, `scores` receives the
+// block records, three planes of T rows of ld blocks: the largest score,
+// the second largest and (as int32) the tile of the largest, ranked as the
+// key order ranks (-0 as +0, NaN lowest: a block of NaN scores records
+// -inf); keys past the range count as NaN.  The work-group's first key kb must then be a
+// multiple of kBlockKeys.
 template <int kHT, bool kPack, bool kCausal, bool kBlockMax = false>
 __device__ __forceinline__ void prefill_unit(
     KeyChunks &kbuf, KeyScales &ks_lds, const uint8_t *__restrict__ q,
@@ -351,9 +354,13 @@ __device__ __forceinline__ void prefill_unit(
     // Block-maximum mode: the work-group's blocks start at column kb / 32.
     const int out_col0 = kBlockMax ? kb / kBlockKeys * kKeysPerTile : kb;
     const int out_cols = kBlockMax ? (ke - kb + kBlockKeys - 1) / kBlockKeys * kKeysPerTile : ke - kb;
-    const __amdgpu_buffer_rsrc_t out = uniform_rsrc(
-        scores + (tok_ok ? t : 0) * ld + out_col0,
-        tok_ok ? (uint32_t)(((int64_t)(tok_rows - 1) * ld + out_cols) * 4) : 0u);
+    const uint32_t out_bytes = tok_ok ? (uint32_t)(((int64_t)(tok_rows - 1) * ld + out_cols) * 4) : 0u;
+    float *const out_base = scores + (tok_ok ? t : 0) * ld + out_col0;
+    const __amdgpu_buffer_rsrc_t out = uniform_rsrc(out_base, out_bytes);
+    // Block-maximum mode: the second and third record planes.
+    const int64_t plane = kBlockMax ? (int64_t)T * ld : 0;
+    const __amdgpu_buffer_rsrc_t out2 = uniform_rsrc(out_base + plane, kBlockMax ? out_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t out3 = uniform_rsrc(out_base + 2 * plane, kBlockMax ? out_bytes : 0u);
     const int key_count = ke - kb;
     uint32_t row_off[kPack ? 4 * kHT : 1];
     // Causal: a store of column kb + n writes -inf unless n < vis_rel (the
@@ -384,10 +391,25 @@ __device__ __forceinline__ void prefill_unit(
     float part[kParts];
     // Block-maximum mode: running maxima of the lane's current block, one
     // per score the lane produces per tile.
-    float bmx[kPack ? kParts : 1];
+    constexpr int kRecs = kPack ? kParts : 1;
+    float bm1[kRecs], bm2[kRecs];
+    int bat[kRecs];
 #pragma unroll
-    for (int g = 0; g < (kPack ? kParts : 1); ++g)
-        bmx[g] = -__builtin_huge_valf();
+    for (int g = 0; g < kRecs; ++g) {
+        bm1[g] = -__builtin_huge_valf();
+        bm2[g] = -__builtin_huge_valf();
+        bat[g] = 0;
+    }
+    // Fold score v of tile `tile` (of its block) into record g.  The IEEE
+    // compare already ranks as the key order does: -0 equals +0, and a NaN
+    // never wins (nor does it enter the second largest through the IEEE
+    // maximum); strict > keeps the earlier (lower) column on a tie.
+    auto record = [&](int g, float v, int tile) {
+        const bool gt = v > bm1[g];
+        bm2[g] = gt ? bm1[g] : __builtin_fmaxf(bm2[g], v);
+        bm1[g] = gt ? v : bm1[g];
+        bat[g] = gt ? tile : bat[g];
+    };
     auto part_of = [](int e) { return kPack ? e / 4 : e % 4; };
     auto first_of_part = [](int e) { return kPack ? e % 4 == 0 : e < 4; };
     auto add_term = [&](int e) {
@@ -423,7 +445,7 @@ __device__ __forceinline__ void prefill_unit(
             for (int g = 0; g < kParts; ++g) {
                 float v = hks * part[g];
                 if constexpr (kBlockMax) {
-                    bmx[g] = __builtin_fmaxf(bmx[g], v);
+                    record(g, v, (n_rel / kKeysPerTile) % kBlockTiles);
                     continue;
                 }
                 if constexpr (kCausal)
@@ -440,27 +462,26 @@ __device__ __forceinline__ void prefill_unit(
         const uint32_t off = (half == 0 && n_rel >= 0) ? (uint32_t)(n_rel + col) * 4u : kDropped;
         float v = ks * (0.5f * total);
         if constexpr (kBlockMax) {
-            bmx[0] = __builtin_fmaxf(bmx[0], v);
+            record(0, v, (n_rel / kKeysPerTile) % kBlockTiles);
             return;
         }
         if constexpr (kCausal)
             v = n_rel + col < vis_rel[0] ? v : -INFINITY;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), out, off, 0, 0);
     };
-    // Block-maximum mode: store the maxima of the block holding the tile
+    // Block-maximum mode: store the records of the block holding the tile
     // whose first key is n_rel, and start the next block.
     auto flush_blocks = [&](int n_rel) {
         const uint32_t boff = (uint32_t)(n_rel / kBlockKeys * kKeysPerTile + col) * 4u;
-        if constexpr (kPack) {
 #pragma unroll
-            for (int g = 0; g < kParts; ++g) {
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bmx[g]), out, row_off[g] + boff, 0, 0);
-                bmx[g] = -__builtin_huge_valf();
-            }
-        } else {
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bmx[0]), out,
-                                                  half == 0 ? boff : kDropped, 0, 0);
-            bmx[0] = -__builtin_huge_valf();
+        for (int g = 0; g < kRecs; ++g) {
+            const uint32_t off = kPack ? row_off[g] + boff : (half == 0 ? boff : kDropped);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bm1[g]), out, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bm2[g]), out2, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)bat[g], out3, off, 0, 0);
+            bm1[g] = -__builtin_huge_valf();
+            bm2[g] = -__builtin_huge_valf();
+            bat[g] = 0;
         }
     };
 
@@ -698,24 +719,24 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_balanced_k
 
 // ---------------------------------------------------------------------------
 // Fused top-16 of prefill score rows (indexer_prefill_topk16), without the
-// score matrix.  Three passes:
+// score matrix.  Two passes:
 //  1. the score kernel in block-maximum mode writes each token's block
-//     maxima (kBlockKeys);
-//  2. topk16_select picks each token's 16 best blocks; the 16th of their
-//     maxima, B16, bounds the token's 16th best score from below, since the
-//     16 blocks hold 16 distinct keys scoring at least B16;
-//  3. this kernel rescores, with the score kernel's arithmetic, the blocks
-//     whose maximum reaches B16 (no other block holds a key scoring B16 or
-//     more), keeps the keys scoring at least B16 (among them the best 16),
-//     and sorts those by the full key order.
-// Rescoring gives the very bits the score kernel computes: the same f16
+//     records (kBlockKeys): largest score, its tile, second largest;
+//  2. this kernel takes a bar every key of the best 16 reaches -- the 16th
+//     largest of its lanes' maxima of the blocks' largest scores -- and
+//     keeps every key scoring at least the bar: a block can hold one only if
+//     its largest score reaches the bar; if its second largest does not,
+//     that key is the largest, known from the record; otherwise the block's
+//     keys are recomputed with the score kernel's arithmetic.  The kept keys
+//     are sorted by the full key order.
+// Recomputing gives the very bits the score kernel computes: the same f16
 // operands in the same MFMA (each accumulator element depends only on its
 // own row and column), eight K steps in the same order, and the same
 // epilogue operations in the same order.
 // ---------------------------------------------------------------------------
 constexpr int kRescoreWaves = 4;
 constexpr int kSurvCap = 256;    // survivors a token holds before compacting to its best 16
-constexpr int kCandBatch = 4;    // candidate blocks whose keys are loaded together
+constexpr int kCandCap = 1024;   // candidate blocks listed before they are settled
 
 // Wave maximum of a 64-bit value (butterfly over the lane distances).
 template <int J>
@@ -770,11 +791,11 @@ template <int kHT, bool kPack>
 __global__ __launch_bounds__(kRescoreWaves * kWave) void prefill_topk_rescore_kernel(
     const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
     const uint8_t *__restrict__ k, const float *__restrict__ k_scale, int32_t T, int32_t H,
-    int32_t N, const float *__restrict__ bmax, int32_t nblocks,
-    const int32_t *__restrict__ best_blocks, int32_t *__restrict__ out, int64_t out_stride)
+    int32_t N, const float *__restrict__ bmax, int32_t nblocks, int32_t *__restrict__ out,
+    int64_t out_stride)
 {
     __shared__ uint64_t surv[kRescoreWaves][kSurvCap];
-    __shared__ int32_t cand[kRescoreWaves][kWave];
+    __shared__ int32_t cand[kRescoreWaves][kCandCap];
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int col = lane & 31;
@@ -809,7 +830,7 @@ __global__ __launch_bounds__(kRescoreWaves * kWave) void prefill_topk_rescore_ke
     }
     // The score of key `n` of lane col (lanes 0..31): the score kernel's
     // epilogue, term for term.
-    auto score_of = [&](const uint2 (&kr)[8], float ks) {
+    auto score_of = [&](const uint2 (&kr)[8], float ks) __attribute__((always_inline)) {
         v16f acc[kTiles];
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
@@ -846,68 +867,184 @@ __global__ __launch_bounds__(kRescoreWaves * kWave) void prefill_topk_rescore_ke
         }
     };
 
-    // B16 (the best blocks come from topk16_select: 16 valid ids, since a
-    // row has at least 32 blocks).
-    const int32_t b16 = best_blocks[t * kTopk + kTopk - 1];
-    const float *brow = bmax + t * nblocks;
-    uint32_t thr = key_hi(b16 >= 0 && b16 < nblocks ? brow[b16] : -__builtin_huge_valf(), false);
-    int count = 0;
-    for (int base = 0; base < nblocks; base += kWave) {
-        const int b = base + lane;
-        const bool is_cand = b < nblocks && key_hi(brow[b], false) >= thr;
-        const uint64_t mask = __ballot(is_cand);
-        if (is_cand)
-            cl[__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u))] = b;
-        const int nc = lanes_set(mask);
-        wave_lds_sync();
-        for (int j0 = 0; j0 < nc; j0 += kCandBatch) {
-            uint2 kr[kCandBatch][8];
-            float ksv[kCandBatch];
-            int64_t nk[kCandBatch];
+    // Block records of the token: largest score, second largest, tile of the
+    // largest (three planes of [T, nblocks]).
+    const int64_t plane = (int64_t)T * nblocks;
+    const float *m1row = bmax + t * nblocks;
+    const float *m2row = m1row + plane;
+    const int32_t *atrow = reinterpret_cast<const int32_t *>(m1row + 2 * plane);
+    const uint32_t kNegInfHi = key_hi(-__builtin_huge_valf(), false);
+
+    // The bar: the 16th largest of the 64 lanes' maxima of the blocks'
+    // largest scores (in key order; lane l holds blocks l, l + 64, ...).
+    // The 16 lanes reaching it hold 16 distinct blocks, hence 16 distinct
+    // keys, scoring at least that much, so no key below it is among the
+    // best 16 (a row has at least 32 blocks, so the 16 lanes are real).
+    // Rows of up to kWin windows keep their largest scores in registers
+    // for the candidate scan below; longer rows read them again.
+    // Lane l holds blocks base + 256 w + 4 l + j (j < 4), loaded 16 bytes at
+    // a time (nblocks is a multiple of 32, so a group of four is whole).
+    constexpr int kWin = kTiles == 2 ? 2 : 8;
+    constexpr int kStep = kWin * 4 * kWave;
+    const bool one_step = nblocks <= kStep;
+    uint32_t rh[kWin][4];
+    uint32_t lmax = 0;   // below every key's high word
+    auto load_step = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
-            for (int cb = 0; cb < kCandBatch; ++cb) {
-                const int blk = j0 + cb < nc ? cl[j0 + cb] : -1;
-                const int64_t n = blk >= 0 ? (int64_t)(blk / kKeysPerTile) * kBlockKeys + blk % kKeysPerTile +
-                                                 (int64_t)kKeysPerTile * col
-                                           : (int64_t)N;
-                const bool live = n < N;
-                nk[cb] = n;
-                const uint2 *src = reinterpret_cast<const uint2 *>(k + (live ? n : 0) * kDepth + 8 * half);
-#pragma unroll
-                for (int st = 0; st < 8; ++st)
-                    kr[cb][st] = live ? src[2 * st] : make_uint2(0u, 0u);
-                ksv[cb] = live ? k_scale[n] : __builtin_nanf("");
-            }
-#pragma unroll
-            for (int cb = 0; cb < kCandBatch; ++cb) {
-                if (j0 + cb >= nc)
-                    break;
-                const float v = score_of(kr[cb], ksv[cb]);
-                const uint32_t hi = key_hi(v, false);
-                const bool keep = half == 0 && nk[cb] < N && hi >= thr;
-                const uint64_t km = __ballot(keep);
-                const int nkeep = lanes_set(km);
-                if (count + nkeep > kSurvCap) {
-                    // Compact to the best 16 and raise the bar to the 16th.
-                    wave_lds_sync();
-                    const uint64_t best = best16_of_list(list, count, lane);
-                    wave_lds_sync();
-                    if (lane < kTopk)
-                        list[lane] = best;
-                    const uint32_t hi16 = __builtin_amdgcn_readlane((uint32_t)(best >> 32), kTopk - 1);
-                    thr = hi16 > thr ? hi16 : thr;
-                    count = kTopk;
-                    wave_lds_sync();
-                }
-                if (keep)
-                    list[count + __builtin_amdgcn_mbcnt_hi((uint32_t)(km >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)km, 0u))] =
-                        make_key(hi, (int)nk[cb]);
-                count += nkeep;
-            }
+        for (int w = 0; w < kWin; ++w) {
+            const int b = base + w * 4 * kWave + 4 * lane;
+            float4 v = make_float4(-__builtin_huge_valf(), 0.f, 0.f, 0.f);
+            if (b < nblocks)
+                v = *reinterpret_cast<const float4 *>(m1row + b);
+            const bool in = b < nblocks;
+            rh[w][0] = in ? key_hi(v.x, false) : 0u;
+            rh[w][1] = in ? key_hi(v.y, false) : 0u;
+            rh[w][2] = in ? key_hi(v.z, false) : 0u;
+            rh[w][3] = in ? key_hi(v.w, false) : 0u;
         }
-        wave_lds_sync();   // before the next window's ids overwrite cl
+    };
+    for (int base = 0; base < nblocks; base += kStep) {
+        load_step(base);
+#pragma unroll
+        for (int w = 0; w < kWin; ++w)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                lmax = rh[w][j] > lmax ? rh[w][j] : lmax;
     }
+    uint32_t thr = __builtin_amdgcn_readlane(wave_sort_desc<kWave>(lmax, lane), kTopk - 1);
+    int count = 0;
+
+    // Append the keys of the lanes with `keep` to the survivor list,
+    // compacting it to its best 16 first if they would not fit (the bar then
+    // rises to the 16th).
+    auto append = [&](bool keep, uint64_t key) __attribute__((always_inline)) {
+        const uint64_t km = __ballot(keep);
+        const int nkeep = lanes_set(km);
+        if (count + nkeep > kSurvCap) {
+            wave_lds_sync();
+            const uint64_t best = best16_of_list(list, count, lane);
+            wave_lds_sync();
+            if (lane < kTopk)
+                list[lane] = best;
+            const uint32_t hi16 = __builtin_amdgcn_readlane((uint32_t)(best >> 32), kTopk - 1);
+            thr = hi16 > thr ? hi16 : thr;
+            count = kTopk;
+            wave_lds_sync();
+        }
+        if (keep)
+            list[count + __builtin_amdgcn_mbcnt_hi((uint32_t)(km >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)km, 0u))] = key;
+        count += nkeep;
+    };
+
+    // Keys of candidate blocks cl[j0 .. j0 + kBatch) (lane col: the block's
+    // key 1024 (b / 32) + b % 32 + 32 col; n = N past the list or the keys).
+    constexpr int kBatch = 2;
+    struct Batch {
+        uint2 kr[kBatch][8];
+        float ks[kBatch];
+        int64_t n[kBatch];
+    };
+    auto load_batch = [&](int j0, int nc, Batch &bt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int cb = 0; cb < kBatch; ++cb) {
+            const int blk = j0 + cb < nc ? cl[j0 + cb] : -1;
+            const int64_t n = blk >= 0 ? (int64_t)(blk / kKeysPerTile) * kBlockKeys + blk % kKeysPerTile +
+                                             (int64_t)kKeysPerTile * col
+                                       : (int64_t)N;
+            const bool live = n < N;
+            bt.n[cb] = n;
+            const uint2 *src = reinterpret_cast<const uint2 *>(k + (live ? n : 0) * kDepth + 8 * half);
+#pragma unroll
+            for (int st = 0; st < 8; ++st)
+                bt.kr[cb][st] = live ? src[2 * st] : make_uint2(0u, 0u);
+            bt.ks[cb] = live ? k_scale[n] : __builtin_nanf("");
+        }
+    };
+    // Score a loaded batch and keep the keys that reach the bar.
+    auto run_batch = [&](int j0, int nc, const Batch &bt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int cb = 0; cb < kBatch; ++cb) {
+            if (j0 + cb >= nc)
+                break;
+            const float v = score_of(bt.kr[cb], bt.ks[cb]);
+            const uint32_t hi = key_hi(v, false);
+            append(half == 0 && bt.n[cb] < N && hi >= thr, make_key(hi, (int)bt.n[cb]));
+        }
+    };
+    // The blocks listed in cl[0, nc), two batches in flight: the next
+    // batch's keys load while this one is scored.
+    auto rescore = [&](int nc) __attribute__((always_inline)) {
+        Batch x, y;
+        load_batch(0, nc, x);
+        for (int j0 = 0; j0 < nc; j0 += 2 * kBatch) {
+            load_batch(j0 + kBatch, nc, y);
+            run_batch(j0, nc, x);
+            if (j0 + kBatch >= nc)
+                break;
+            load_batch(j0 + 2 * kBatch, nc, x);
+            run_batch(j0 + kBatch, nc, y);
+        }
+    };
+
+    // A block whose largest score reaches the bar is a candidate.  If its
+    // second largest is below the bar, its only key that can count is the
+    // largest, whose score and column the record gives: it joins the
+    // survivors directly.  Otherwise (two or more keys at the bar, or a
+    // block of -inf / NaN scores) its keys are rescored.  Candidates are
+    // listed in cl and settled (their other two records read, the direct
+    // ones kept, the others compacted to the front of cl and rescored)
+    // when the list could overflow and at the end.
+    auto settle = [&](int nc) __attribute__((always_inline)) {
+        int na = 0;
+        for (int g0 = 0; g0 < nc; g0 += kWave) {
+            const bool in = g0 + lane < nc;
+            const int b = in ? cl[g0 + lane] : 0;
+            const float r1 = m1row[b], r2 = m2row[b];
+            const int at = atrow[b];
+            wave_lds_sync();   // cl is read before it is rewritten below
+            const uint32_t h1 = key_hi(r1, false);
+            const bool direct = in && h1 > kNegInfHi && key_hi(r2, false) < thr;
+            const int64_t colk = (int64_t)(b / kKeysPerTile) * kBlockKeys + b % kKeysPerTile +
+                                 (int64_t)kKeysPerTile * at;
+            append(direct, make_key(h1, (int)colk));
+            const bool again = in && !direct;
+            const uint64_t mask = __ballot(again);
+            if (again)
+                cl[na + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u))] = b;
+            na += lanes_set(mask);
+            wave_lds_sync();
+        }
+        if (na > 0)
+            rescore(na);
+        wave_lds_sync();
+    };
+    int nc = 0;
+    for (int base = 0; base < nblocks; base += kStep) {
+        if (!one_step)
+            load_step(base);
+#pragma unroll
+        for (int w = 0; w < kWin; ++w) {
+            if (nc > kCandCap - 4 * kWave) {
+                settle(nc);
+                nc = 0;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool is_cand = rh[w][j] >= thr;   // 0 (no block) never reaches the bar
+                const uint64_t mask = __ballot(is_cand);
+                if (is_cand)
+                    cl[nc + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u))] =
+                        base + w * 4 * kWave + 4 * lane + j;
+                nc += lanes_set(mask);
+            }
+            wave_lds_sync();
+        }
+    }
+    if (nc > 0)
+        settle(nc);
     const uint64_t best = best16_of_list(list, count, lane);
     if (lane < kTopk)
         out[t * out_stride + lane] = best != 0 ? key_col(best) : -1;
@@ -1015,17 +1152,15 @@ int64_t prefill_topk16_blocks(int32_t N)
 
 hipError_t launch_prefill_topk16(const uint8_t *q, const float *q_scale, const uint8_t *k,
                                  const float *k_scale, int32_t T, int32_t H, int32_t N, int32_t *out,
-                                 int64_t out_stride, float *bmax, int32_t *best_blocks, int num_cus,
-                                 hipStream_t stream)
+                                 int64_t out_stride, float *bmax, hipStream_t stream)
 {
     if (H > kSmallHeads || T < 1 || N < 1)
         return hipErrorInvalidValue;
     const int64_t nblocks = prefill_topk16_blocks(N);
-    if (nblocks > kTopkMaxWidth)
-        return hipErrorInvalidValue;
-    // Pass 1: block maxima, with the score kernel's launch shape (about one
+    // Pass 1: block records, with the score kernel's launch shape (about one
     // work-group per compute unit), key splits in whole blocks of 1,024.
-    const bool pack = H <= kPackHeads && nblocks <= kPackMaxLd;
+    const int64_t ld = nblocks;                              // record planes of [T, nblocks]
+    const bool pack = H <= kPackHeads && ld <= kPackMaxLd;
     const int pack_tiles = T > 8 * kH64Waves ? 2 : 1;
     const int64_t tokens_per_group = (int64_t)kH64Waves * (pack ? 8 * pack_tiles : 1);
     const int64_t groups = ((int64_t)T + tokens_per_group - 1) / tokens_per_group;
@@ -1044,35 +1179,31 @@ hipError_t launch_prefill_topk16(const uint8_t *q, const float *q_scale, const u
     const RaggedBatch none{};
     if (pack && pack_tiles == 2)
         hipLaunchKernelGGL((score_prefill_h64_kernel<2, true, false, true>), grid, block, 0, stream, q,
-                           q_scale, k, k_scale, T, H, N, (int32_t)keys_per_group, bmax, nblocks, none);
+                           q_scale, k, k_scale, T, H, N, (int32_t)keys_per_group, bmax, ld, none);
     else if (pack)
         hipLaunchKernelGGL((score_prefill_h64_kernel<1, true, false, true>), grid, block, 0, stream, q,
-                           q_scale, k, k_scale, T, H, N, (int32_t)keys_per_group, bmax, nblocks, none);
+                           q_scale, k, k_scale, T, H, N, (int32_t)keys_per_group, bmax, ld, none);
     else if (H <= 32)
         hipLaunchKernelGGL((score_prefill_h64_kernel<1, false, false, true>), grid, block, 0, stream, q,
-                           q_scale, k, k_scale, T, H, N, (int32_t)keys_per_group, bmax, nblocks, none);
+                           q_scale, k, k_scale, T, H, N, (int32_t)keys_per_group, bmax, ld, none);
     else
         hipLaunchKernelGGL((score_prefill_h64_kernel<2, false, false, true>), grid, block, 0, stream, q,
-                           q_scale, k, k_scale, T, H, N, (int32_t)keys_per_group, bmax, nblocks, none);
-    hipError_t e = hipGetLastError();
+                           q_scale, k, k_scale, T, H, N, (int32_t)keys_per_group, bmax, ld, none);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    // Pass 2: the 16 best blocks of every token.
-    e = launch_topk16(bmax, nblocks, T, (int32_t)nblocks, nullptr, nullptr, nullptr, nullptr,
-                      best_blocks, kTopk, num_cus, stream);
-    if (e != hipSuccess)
-        return e;
-    // Pass 3: rescoring and the exact selection.
+    // Pass 2: the bar, the candidates, rescoring where needed and the exact
+    // selection.
     const dim3 g3((uint32_t)(((int64_t)T + kRescoreWaves - 1) / kRescoreWaves)), b3(kRescoreWaves * kWave);
     if (pack)
         hipLaunchKernelGGL((prefill_topk_rescore_kernel<1, true>), g3, b3, 0, stream, q, q_scale, k,
-                           k_scale, T, H, N, bmax, (int32_t)nblocks, best_blocks, out, out_stride);
+                           k_scale, T, H, N, bmax, (int32_t)nblocks, out, out_stride);
     else if (H <= 32)
         hipLaunchKernelGGL((prefill_topk_rescore_kernel<1, false>), g3, b3, 0, stream, q, q_scale, k,
-                           k_scale, T, H, N, bmax, (int32_t)nblocks, best_blocks, out, out_stride);
+                           k_scale, T, H, N, bmax, (int32_t)nblocks, out, out_stride);
     else
         hipLaunchKernelGGL((prefill_topk_rescore_kernel<2, false>), g3, b3, 0, stream, q, q_scale, k,
-                           k_scale, T, H, N, bmax, (int32_t)nblocks, best_blocks, out, out_stride);
+                           k_scale, T, H, N, bmax, (int32_t)nblocks, out, out_stride);
     return hipGetLastError();
 }
 

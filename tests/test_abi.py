@@ -134,10 +134,10 @@ def _workspace(lib, T, N):
 
 
 def test_prefill_topk16_workspace_size(lib):
-    # Block maxima [T, 32 ceil(N / 1024)] float32 padded to 256 bytes, then [T, 16] int32.
-    assert _workspace(lib, 2048, 65536) == 2048 * 2048 * 4 + 2048 * 64
-    assert _workspace(lib, 5, 1) == 768 + 5 * 64
-    assert _workspace(lib, 3, 1025) == 3 * 64 * 4 + 3 * 64
+    # Block records: three planes [T, 32 ceil(N / 1024)] of 4 bytes each.
+    assert _workspace(lib, 2048, 65536) == 2048 * 3 * 2048 * 4
+    assert _workspace(lib, 5, 1) == 5 * 3 * 32 * 4
+    assert _workspace(lib, 3, 1025) == 3 * 3 * 64 * 4
     assert _workspace(lib, 0, 7) == 0
     assert _workspace(lib, -1, 7) < 0
     assert _workspace(lib, 4, 0) < 0
