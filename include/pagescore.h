@@ -42,6 +42,7 @@ extern "C" {
 #define PAGESCORE_OK 0
 #define PAGESCORE_EINVAL (-22)  /* an argument failed a host-side check      */
 #define PAGESCORE_ELAUNCH (-5)  /* a kernel launch failed; see last_hip_error */
+#define PAGESCORE_ENOSPACE (-28) /* more scratch needed than the fixed array holds */
 
 #define PAGESCORE_PAGE_TOKENS 128
 #define PAGESCORE_DEPTH 128
@@ -261,6 +262,24 @@ int indexer_prefill_topk16(const uint8_t *q, const float *q_scale, const uint8_t
                            const float *k_scale, int32_t T, int32_t H, int32_t N, int32_t *out,
                            int64_t out_stride, void *workspace, int64_t workspace_bytes,
                            void *stream);
+
+/*
+ * indexer_prefill_topk16_noalloc -- indexer_prefill_topk16 for callers that
+ * cannot allocate device memory: code under HIP graph capture, allocation-free
+ * serving loops, harnesses that forbid allocation.  Same arguments (without
+ * the workspace) and the same results; the workspace is instead an array of
+ * PAGESCORE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held from
+ * the library's first use on that GPU until the process ends.
+ * PAGESCORE_ENOSPACE when indexer_prefill_topk16_workspace(T, N) exceeds it
+ * (nothing is enqueued).  Every call on one GPU uses the same array: calls
+ * that can overlap in time on one GPU (different streams or threads) race,
+ * so order them, e.g. on one stream.  The array needs no clearing between
+ * calls (each call writes what it reads).
+ */
+#define PAGESCORE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int indexer_prefill_topk16_noalloc(const uint8_t *q, const float *q_scale, const uint8_t *k,
+                                   const float *k_scale, int32_t T, int32_t H, int32_t N,
+                                   int32_t *out, int64_t out_stride, void *stream);
 
 /*
  * mxfp8_e4m3_quantize -- MXFP8 quantization of bf16 rows, the step after the

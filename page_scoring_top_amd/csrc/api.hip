@@ -1,6 +1,7 @@
 // api.hip -- the exported C ABI (declared in include/pagescore.h): host-side
-// argument checks, then one stream-ordered launch per call.  Nothing here
-// synchronizes with the host or allocates memory.
+// argument checks, then stream-ordered launches.  Nothing here synchronizes
+// with the host or allocates memory (the allocation-free prefill top-16 uses
+// a static device array, below).
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <mutex>
@@ -21,6 +22,43 @@ int launch_status(hipError_t e)
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+// Workspace of indexer_prefill_topk16_noalloc: one array per GPU, held by the
+// loaded code object until the process ends.  Host code never uses its name
+// as an address (it is a host-side stand-in there); the device address comes
+// from hipGetSymbolAddress, once per device, in noalloc_scratch().
+static __device__ __align__(256) uint8_t scratch[PAGESCORE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device (nullptr and the HIP
+// error in *err if it cannot be had).
+void *noalloc_scratch(hipError_t *err)
+{
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {nullptr};
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess)
+        return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void *p = nullptr;
+        *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess)
+            return nullptr;
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
 
 // Compute units of the current device, queried once per device.
 int current_device_cus()
@@ -147,6 +185,28 @@ int indexer_prefill_topk16(const uint8_t *q, const float *q_scale, const uint8_t
                                                           (hipStream_t)stream));
 }
 
+int indexer_prefill_topk16_noalloc(const uint8_t *q, const float *q_scale, const uint8_t *k,
+                                   const float *k_scale, int32_t T, int32_t H, int32_t N,
+                                   int32_t *out, int64_t out_stride, void *stream)
+{
+    if (T < 0 || N < 1 || H < 1 || H > PAGESCORE_PREFILL_TOPK_MAX_HEADS)
+        return PAGESCORE_EINVAL;
+    if (T == 0)
+        return PAGESCORE_OK;
+    if (!q || !aligned16(q) || !q_scale || !k || !aligned16(k) || !k_scale || !out ||
+        out_stride < PAGESCORE_TOPK)
+        return PAGESCORE_EINVAL;
+    if (indexer_prefill_topk16_workspace(T, N) > (int64_t)PAGESCORE_NOALLOC_SCRATCH_BYTES)
+        return PAGESCORE_ENOSPACE;
+    hipError_t err = hipSuccess;
+    void *ws = noalloc_scratch(&err);
+    if (ws == nullptr)
+        return launch_status(err);
+    return launch_status(pagescore::launch_prefill_topk16(q, q_scale, k, k_scale, T, H, N, out,
+                                                          out_stride, static_cast<float *>(ws),
+                                                          (hipStream_t)stream));
+}
+
 int topk16_select(const float *scores, int64_t row_stride, int32_t num_rows, int32_t width,
                   const int32_t *valid_len, const int32_t *force_begin, const int32_t *force_end,
                   const int32_t *append_page, int32_t *out, int64_t out_stride, void *stream)
@@ -189,6 +249,8 @@ const char *pagescore_strerror(int code)
         return "invalid argument (host-side check)";
     case PAGESCORE_ELAUNCH:
         return "kernel launch failed (see pagescore_last_hip_error)";
+    case PAGESCORE_ENOSPACE:
+        return "the call needs more scratch than the library's fixed array holds";
     default:
         return "unknown error code";
     }

@@ -32,7 +32,8 @@ def test_header_declares_every_call():
     fns = declared_functions()
     for name in ("nvfp4_index_k_dequant", "indexer_score_decode", "indexer_score_prefill",
                  "indexer_score_prefill_ragged", "topk16_select", "mxfp8_e4m3_quantize",
-                 "indexer_prefill_topk16", "indexer_prefill_topk16_workspace"):
+                 "indexer_prefill_topk16", "indexer_prefill_topk16_workspace",
+                 "indexer_prefill_topk16_noalloc"):
         assert name in fns
 
 
@@ -172,6 +173,23 @@ def test_prefill_topk16_host_checks(lib):
     assert _prefill_topk(lib, ws=None) == EINVAL
     assert _prefill_topk(lib, ws=P(0x10010)) == EINVAL          # 16- but not 256-byte aligned
     assert _prefill_topk(lib, wsb=_workspace(lib, 4, 100) - 1) == EINVAL
+
+
+def test_prefill_topk16_noalloc_host_checks(lib):
+    # Refusals only: nothing here reaches the device.
+    f = lib.indexer_prefill_topk16_noalloc
+    f.argtypes = [P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int64, P]
+    f.restype = ctypes.c_int
+
+    def call(T=4, H=4, N=100, q=FAKE, os=16):
+        return f(q, FAKE, FAKE, FAKE, T, H, N, FAKE, os, None)
+    assert call(T=0) == 0
+    assert call(H=0) == EINVAL
+    assert call(N=0) == EINVAL
+    assert call(q=ODD) == EINVAL
+    assert call(os=15) == EINVAL
+    # 4,096 tokens x 2,048 blocks x 12 bytes = 96 MiB > the 64 MiB array.
+    assert call(T=4096, N=65536) == -28
 
 
 def _topk(lib, **kw):
