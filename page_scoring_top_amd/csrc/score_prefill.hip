@@ -400,14 +400,16 @@ __device__ __forceinline__ void prefill_unit(
         bm2[g] = -__builtin_huge_valf();
         bat[g] = 0;
     }
-    // Fold score v of tile `tile` (of its block) into record g.  The IEEE
-    // compare already ranks as the key order does: -0 equals +0, and a NaN
-    // never wins (nor does it enter the second largest through the IEEE
-    // maximum); strict > keeps the earlier (lower) column on a tie.
+    // Fold score v of tile `tile` (of its block) into record g.  With
+    // bm2 <= bm1, the new second largest is the median of (bm2, bm1, v)
+    // (bm1 again on a tie), one v_med3_f32; the IEEE compare and maximum
+    // already rank as the key order does: -0 equals +0, a NaN never wins,
+    // and v_med3_f32 with a NaN operand returns the minimum of the others
+    // (bm2 here).  Strict > keeps the earlier (lower) column on a tie.
     auto record = [&](int g, float v, int tile) {
         const bool gt = v > bm1[g];
-        bm2[g] = gt ? bm1[g] : __builtin_fmaxf(bm2[g], v);
-        bm1[g] = gt ? v : bm1[g];
+        bm2[g] = __builtin_amdgcn_fmed3f(bm2[g], bm1[g], v);
+        bm1[g] = __builtin_fmaxf(bm1[g], v);
         bat[g] = gt ? tile : bat[g];
     };
     auto part_of = [](int e) { return kPack ? e / 4 : e % 4; };

@@ -142,3 +142,26 @@ def test_nvfp4_prefill_chain():
     ones = torch.ones(N, dtype=torch.float32, device="cuda")
     _check("nvfp4 2048x4x65536", dev(d.q), dev(d.q_scale), keys.view(-1, 128)[:N].contiguous(), ones,
            oracle_rows=8)
+
+
+@pytest.mark.parametrize("H", [1, 4, 64])
+def test_two_best_keys_in_one_block_with_nan_between(H):
+    """A block (the keys 5 + 32 i of the first 1,024) holding the row's two
+    best keys, at i = 3 and i = 20, with NaN scores at i = 0 and i = 10 of
+    the same block: the block's second largest score must survive the NaNs,
+    or the second best key would be missed.  Every other key scores the
+    same (ties to the lowest columns)."""
+    T, N = 3, 2048
+    one = 0x38                                     # E4M3 1.0: every dot is 128
+    q = np.full((T, H, 128), one, np.uint8)
+    k = np.full((N, 128), one, np.uint8)
+    qs = np.ones((T, H), np.float32)
+    ks = np.ones(N, np.float32)
+    ks[5 + 32 * 3] = 100.0
+    ks[5 + 32 * 20] = 90.0
+    ks[5 + 32 * 0] = np.nan
+    ks[5 + 32 * 10] = np.nan
+    got = host(_fused(dev(q), dev(qs), dev(k), dev(ks)))
+    rest = [c for c in range(N) if c not in (5, 5 + 320, 101, 645)][:14]
+    assert (got == np.array([101, 645] + rest, np.int32)).all(), got[0]
+    _check(f"two best in one block H={H}", dev(q), dev(qs), dev(k), dev(ks), oracle_rows=T)
