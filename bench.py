@@ -381,6 +381,8 @@ def bench_nvfp4_prefill(args):
         gather_call()
         score_call()
         topk_call()
+        ws = ps.prefill_topk16_workspace(T, N, dev)
+        ps.indexer_prefill_topk16(q, qs, keys.view(-1, 128)[:N], ones, out, ws)
         torch.cuda.synchronize()
         print(json.dumps({"profile_pass": True, "workload": "nvfp4-prefill", "copy_bytes": 1 << 30}),
               flush=True)
