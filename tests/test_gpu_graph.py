@@ -109,3 +109,20 @@ def test_prepared_calls_eager_and_in_a_graph():
     own.zero_()
     _replay_check(lambda: call.again()(), [scores, own])
     assert torch.equal(scores, direct) and torch.equal(own, own_d)
+
+
+def test_fused_prefill_topk_in_a_graph():
+    """indexer_prefill_topk16 (two kernels over a workspace) replayed from a
+    graph gives the eager rows every time."""
+    import page_scoring_top_amd as ps
+    T, H, N = 300, 4, 20000
+    p = workloads.prefill_inputs("graph-ptk", 81, T, H, N)
+    q, qs, k, ks = dev(p.q), dev(p.q_scale), dev(p.k), dev(p.k_scale)
+    out = torch.zeros((T, 16), dtype=torch.int32, device="cuda")
+    ws = ps.prefill_topk16_workspace(T, N, "cuda")
+
+    def step():
+        ps.indexer_prefill_topk16(q, qs, k, ks, out, ws)
+
+    announce("graph: fused prefill top-16")
+    _replay_check(step, [out])
