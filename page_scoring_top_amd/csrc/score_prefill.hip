@@ -25,7 +25,10 @@
 // of indexer_score_prefill_ragged, either one unit per work-group of a grid
 // or, for up to 256 sequences with one token per wave, as a balanced
 // schedule: one work-group per compute unit, each taking an equal share of
-// the batch's chunks.  More heads take the general kernel: a
+// the batch's chunks.  It also runs the first pass of the fused top-16
+// (indexer_prefill_topk16), keeping per-block records instead of storing
+// scores; the second pass, prefill_topk_rescore_kernel, selects from them
+// (see the section near the end).  More heads take the general kernel: a
 // work-group converts a few tokens' query rows once into LDS, and each wave
 // takes 32-key tiles, converts them into its B registers and runs every
 // token of the group against them.
