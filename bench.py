@@ -42,7 +42,8 @@ sys.path.insert(0, ROOT)
 METRIC = "index-K GB/s scored (frac of HBM peak) + top-16 rows/s, 500K-token decode"
 HBM_PEAK_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "score_decode_long_counters.txt")
-SCORE_SOURCES = ["csrc/score_decode.hip", "csrc/device_common.hpp", "csrc/nvfp4_lut.hpp"]
+SCORE_SOURCES = ["csrc/score_decode.hip", "csrc/wave_keys.hpp", "csrc/device_common.hpp",
+                 "csrc/nvfp4_lut.hpp"]
 MX_COUNTERS_FILE = os.path.join(ROOT, "profiles", "mxfp8_quant_counters.txt")
 MX_SOURCES = ["csrc/mxfp8.hip", "csrc/device_common.hpp", "csrc/nvfp4_lut.hpp"]
 DQ_COUNTERS_FILE = os.path.join(ROOT, "profiles", "nvfp4_dequant_counters.txt")

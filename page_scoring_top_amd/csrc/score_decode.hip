@@ -46,6 +46,10 @@
 //
 // Scheduling: work-group (x, b) covers request b; each of its waves owns a run
 // of `chunk` consecutive pages (chosen on the host from the batch size).  A
+// batch too large for one round of such runs (ragged batches, whose upper
+// bound of requests x width is far above their real pages) takes the flat
+// schedule instead: the real pages are split evenly over all waves
+// (score_decode_flat_kernel).  A
 // wave issues its first loads -- the request's length, the run's page ids and
 // the query rows -- all at once, so a single memory round trip precedes the
 // first page fetch.  Then it scores the run from one set of page registers
@@ -64,6 +68,7 @@
 // dots, and the page score, NaN; a NaN query byte makes its row NaN.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "wave_keys.hpp"
 
 namespace pagescore {
 
@@ -75,6 +80,9 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kXcds = 8;   // accelerator complex dies of an MI355X, each with its own L2
+// Batches of up to this many requests take the flat schedule (each wave
+// walks the request list once to find its share).
+constexpr int32_t kFlatMaxReqs = 4096;
 
 struct PageRegs {
     u32x4 codes[8];   // per tile: 16 code bytes of token 16*tile + m, chunk g
@@ -404,6 +412,132 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
     }
 }
 
+// The pages [ja, jb) of request b (length seq): its query rows, then runs of
+// up to 64 pages, each run's ids loaded at once and its pages scored through
+// the one set of page registers as in score_decode_kernel.
+__device__ __forceinline__ void score_segment(
+    const uint8_t *__restrict__ kv, int64_t page_stride, int32_t nb32,
+    const int32_t *__restrict__ block_table, int64_t bt_stride, const uint8_t *__restrict__ q,
+    const float *__restrict__ q_scale, int32_t qlen, int32_t width, float *__restrict__ scores,
+    const uint64_t *lut, uint8_t *stage, int b, int32_t seq, int ja, int jb, int lane, int m, int g)
+{
+    RequestRaw qraw;
+    load_request_raw(qraw, q, q_scale, qlen, b, lane, m, g);
+    int32_t id_lane = lane < jb - ja ? block_table[(int64_t)b * bt_stride + ja + lane] : -1;
+    RequestRegs rq;
+    finish_request(rq, qraw, seq, qlen, lane);
+    for (int j0 = ja; j0 < jb; j0 += kWave) {
+        const int j1 = __builtin_amdgcn_readfirstlane(j0 + kWave < jb ? j0 + kWave : jb);
+        if (j0 > ja)
+            id_lane = lane < j1 - j0 ? block_table[(int64_t)b * bt_stride + j0 + lane] : -1;
+        // (j = j1 after a full run of 64 reads lane 0 back; the page is not scored.)
+        auto page_src = [&](int j, bool &ok) -> __amdgpu_buffer_rsrc_t {
+            const int32_t id = __builtin_amdgcn_readlane(id_lane, (j - j0) & (kWave - 1));
+            ok = j < j1 && id >= 0 && id < nb32;
+            return page_rsrc(kv + (int64_t)(ok ? id : 0) * page_stride, ok);
+        };
+        PageRegs pr;
+        bool cur_ok = false;
+        fetch_page(pr, page_src(j0, cur_ok), lane, m, g);
+        for (int j = j0; j < j1; ++j) {
+            bool nxt_ok;
+            const __amdgpu_buffer_rsrc_t nsrc = page_src(j + 1 < j1 ? j + 1 : j1, nxt_ok);
+            uint32_t sc[8];
+            unpack_scales(pr, stage, lane, m, g, sc);
+            pr.scales = __builtin_amdgcn_raw_buffer_load_b128(nsrc, kCodeBytes + 16 * lane, 0, kStreamLoad);
+            float v;
+            score_page(pr, sc, lut, rq, nsrc, lane, m, g, v);
+            if (cur_ok && j < rq.own) {
+                const float s = (v + fabsf(v)) * 0.5f * rq.qs;
+                scores[((int64_t)b * kDecodeRows + store_row(lane)) * width + j] = s;
+            }
+            cur_ok = nxt_ok;
+        }
+    }
+}
+
+// Flat schedule: the batch's real pages, listed request by request, are
+// split into equal shares over every wave of the grid (P w / W onward for
+// wave w of W), whatever the requests' lengths.  A share is one or a few
+// segments of consecutive pages of one request.  Requests are numbered over
+// the waves for their row_own.  A ragged batch then runs in one even round
+// instead of a grid over requests x width whose work-groups past a
+// request's last page exit at once, leaving the real pages in uneven
+// rounds.
+__global__ __launch_bounds__(256, 2) void score_decode_flat_kernel(
+    const uint8_t *__restrict__ kv, int64_t page_stride, int64_t num_blocks,
+    const int32_t *__restrict__ block_table, int64_t bt_stride,
+    const int32_t *__restrict__ seq_lens, const uint8_t *__restrict__ q,
+    const float *__restrict__ q_scale, int32_t num_reqs, int32_t qlen, int32_t width,
+    float *__restrict__ scores, int32_t *__restrict__ row_own)
+{
+    __shared__ uint64_t lut[256];
+    __shared__ __align__(16) uint8_t scale_stage[kWavesPerBlock][1024];
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int m = lane & 15;
+    const int g = lane >> 4;
+    // Work-groups numbered so that every XCD holds a contiguous range of
+    // shares (score lines shared by neighbouring columns stay in one L2).
+    const int G = gridDim.x;
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    const int per = G / kXcds, extra = G % kXcds;
+    const int logical = xcd < extra ? xcd * (per + 1) + slot : extra * (per + 1) + (xcd - extra) * per + slot;
+    const int64_t W = (int64_t)G * kWavesPerBlock;
+    const int64_t w = (int64_t)logical * kWavesPerBlock + wave;
+    lut[tid] = kNvfp4Lut.entry[tid] | ((tid & 0x80) ? 0x8080808080808080ull : 0ull);
+    uint8_t *stage = scale_stage[wave];
+
+    // The batch's pages (the host keeps num_reqs x width below 2^31).
+    int32_t total = 0;
+    for (int b0 = 0; b0 < num_reqs; b0 += kWave)
+        total += b0 + lane < num_reqs ? pages_scored(seq_lens[b0 + lane], width) : 0;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1)
+        total += __shfl_xor(total, d);
+    total = __builtin_amdgcn_readfirstlane(total);
+    const int64_t s0 = (int64_t)total * w / W, s1 = (int64_t)total * (w + 1) / W;
+    if (row_own != nullptr && store_row(lane) >= 0) {
+        for (int64_t b = w; b < num_reqs; b += W)
+            row_own[b * kDecodeRows + store_row(lane)] = decode_own(seq_lens[b], qlen, store_row(lane) / kDecodeHeads);
+    }
+    __syncthreads();   // the table is in LDS
+    if (s0 >= s1)
+        return;
+
+    // The request holding page s0: windows of 64 requests and the inclusive
+    // sums of their page counts.
+    int64_t pos = 0;
+    int b = num_reqs;
+    for (int b0 = 0; b0 < num_reqs; b0 += kWave) {
+        const int bb = b0 + lane;
+        const int n = bb < num_reqs ? pages_scored(seq_lens[bb], width) : 0;
+        const int excl = wave_prefix_sum(n, lane);
+        const int win = __builtin_amdgcn_readlane(excl + n, kWave - 1);
+        if (pos + win <= s0) {
+            pos += win;
+            continue;
+        }
+        const uint64_t mask = __ballot(bb < num_reqs && pos + excl + n > s0);
+        const int first = (int)__builtin_ctzll(mask);
+        b = b0 + first;
+        pos += __builtin_amdgcn_readlane(excl, first);
+        break;
+    }
+    const int32_t nb32 = num_blocks > 0x7FFFFFFF ? 0x7FFFFFFF : (int32_t)num_blocks;
+    for (; b < num_reqs && pos < s1; ++b) {
+        const int32_t seq = __builtin_amdgcn_readfirstlane(seq_lens[b]);
+        const int np = pages_scored(seq, width);
+        const int ja = (int)(s0 > pos ? s0 - pos : 0);
+        const int jb = (int)(s1 - pos < np ? s1 - pos : np);
+        if (ja < jb)
+            score_segment(kv, page_stride, nb32, block_table, bt_stride, q, q_scale, qlen, width, scores,
+                          lut, stage, b, seq, ja, jb, lane, m, g);
+        pos += np;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_score_decode(const uint8_t *kv, int64_t page_stride, int64_t num_blocks,
@@ -418,6 +552,16 @@ hipError_t launch_score_decode(const uint8_t *kv, int64_t page_stride, int64_t n
     // lose more to the last runs than they save on per-run set-up.
     const int64_t max_pages = (int64_t)num_reqs * width;
     const int64_t waves = (int64_t)(num_cus > 0 ? num_cus : 256) * 8;
+    // The grid holds at most 8 pages per wave; a batch whose upper bound of
+    // pages exceeds one round of that (ragged or very large batches) takes
+    // the flat schedule, which splits the real pages evenly instead.
+    if (max_pages > waves * 8 && num_reqs <= kFlatMaxReqs && max_pages <= 0x7FFFFFFF) {
+        const dim3 grid((uint32_t)((num_cus > 0 ? num_cus : 256) * 2));
+        hipLaunchKernelGGL(score_decode_flat_kernel, grid, dim3(256), 0, stream, kv, page_stride,
+                           num_blocks, block_table, bt_stride, seq_lens, q, q_scale, num_reqs, qlen,
+                           width, scores, row_own);
+        return hipGetLastError();
+    }
     int64_t chunk = (max_pages + waves - 1) / waves;
     chunk = chunk < 1 ? 1 : (chunk > 8 ? 8 : chunk);
     const int64_t gx = ((int64_t)width + chunk * kWavesPerBlock - 1) / (chunk * kWavesPerBlock);

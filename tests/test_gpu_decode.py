@@ -203,3 +203,26 @@ def test_most_requests_in_one_call():
     s, own = run_decode(d)
     n = check_full(d, s, own, pooled=True)
     assert n == (R // 64 + (1 if R % 64 > 5 else 0)) * 32 * 2
+
+
+@pytest.mark.timeout(900)
+def test_flat_schedule_with_shares_over_64_pages():
+    """A batch over one round of 8 pages per wave takes the flat schedule;
+    here 38 requests of 3,492 scored pages each (132,696 pages, more than 64
+    per wave on 2,048 waves), so each wave scores runs of 64 pages and some
+    shares cross a request boundary.  Pages come from a shared pool of 4,096
+    (ids repeat); every stored score is compared."""
+    R, seq_len = 38, 447_000
+    W = (seq_len + 127) // 128
+    rng = np.random.default_rng(43)
+    base = workloads.decode_inputs("flat-pool", 43, [300], qlen=8, width=4, pool_pages=4096)
+    kv = base.kv_cache
+    bt = rng.integers(0, kv.shape[0], size=(R, W), dtype=np.int32)
+    q = workloads.e4m3_bytes_from_normal(rng, (R, 8, 4, 128))
+    qs = rng.uniform(0.5, 2.0, size=(R, 8, 4)).astype(np.float32)
+    seq = np.full(R, seq_len, np.int32)
+    d = workloads.DecodeInputs("flat-long-runs", kv, bt, seq, q, qs, 8, W, R)
+    announce("decode flat schedule, 38 x 3,492 pages")
+    s, own = run_decode(d)
+    n = check_full(d, s, own, pooled=True)
+    assert n == R * 32 * (W - 1)
