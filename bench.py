@@ -48,8 +48,8 @@ MX_COUNTERS_FILE = os.path.join(ROOT, "profiles", "mxfp8_quant_counters.txt")
 MX_SOURCES = ["csrc/mxfp8.hip", "csrc/device_common.hpp", "csrc/nvfp4_lut.hpp"]
 DQ_COUNTERS_FILE = os.path.join(ROOT, "profiles", "nvfp4_dequant_counters.txt")
 DQ_SOURCES = ["csrc/dequant.hip", "csrc/device_common.hpp", "csrc/nvfp4_lut.hpp"]
-PREFILL_SOURCES = ["csrc/score_prefill.hip", "csrc/wave_keys.hpp", "csrc/device_common.hpp",
-                   "csrc/nvfp4_lut.hpp"]
+PREFILL_SOURCES = ["csrc/score_prefill.hip", "csrc/causal_share.hpp", "csrc/wave_keys.hpp",
+                   "csrc/device_common.hpp", "csrc/nvfp4_lut.hpp"]
 TOPK_SOURCES = ["csrc/topk16.hip", "csrc/wave_keys.hpp", "csrc/device_common.hpp", "csrc/nvfp4_lut.hpp"]
 
 

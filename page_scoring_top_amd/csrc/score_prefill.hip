@@ -33,6 +33,7 @@
 // takes 32-key tiles, converts them into its B registers and runs every
 // token of the group against them.
 #include "device_common.hpp"
+#include "causal_share.hpp"
 #include "launch.hpp"
 #include "wave_keys.hpp"
 
@@ -170,6 +171,33 @@ struct RaggedBatch {
     int32_t width;            // score columns per row
 };
 
+// Sequence s of a ragged batch cut to the buffers: query rows
+// [row0, row0 + q_len) of [0, T) and keys [k0, k0 + klen) of [0, N) (a key
+// slice leaving the buffer keeps the part inside it; one starting outside
+// it has no keys).
+struct SeqSlice {
+    int32_t row0, q_len, k0, klen;
+};
+
+// The slice of a sequence whose batch entries are q_start = qa, qb (its
+// own and the next), k_start = k0 and k_len = kl.
+__device__ __forceinline__ SeqSlice slice_of(int32_t qa, int32_t qb, int32_t k0, int32_t kl, int32_t T,
+                                             int32_t N)
+{
+    int64_t a0 = qa, a1 = qb;
+    a0 = a0 < 0 ? 0 : (a0 > T ? T : a0);
+    a1 = a1 < a0 ? a0 : (a1 > T ? T : a1);
+    const bool inside = k0 >= 0 && k0 <= N;
+    const int64_t room = (int64_t)N - k0;
+    const int64_t n = !inside ? 0 : (kl > room ? room : (kl < 0 ? 0 : kl));
+    return SeqSlice{(int32_t)a0, (int32_t)(a1 - a0), inside ? k0 : 0, (int32_t)n};
+}
+
+__device__ __forceinline__ SeqSlice seq_slice(const RaggedBatch &rb, int s, int32_t T, int32_t N)
+{
+    return slice_of(rb.q_start[s], rb.q_start[s + 1], rb.k_start[s], rb.k_len[s], T, N);
+}
+
 constexpr int kH64Waves = 8;                                  // waves per work-group
 constexpr int kChunkKeys = 128;
 constexpr int kChunkBufs = 3;
@@ -213,7 +241,7 @@ typedef uint8_t KeyChunks[kChunkBufs][kChunkKeys * kKeyRowBytes];
 typedef float KeyScales[kChunkBufs][kChunkKeys];
 
 // One unit of work-group work: the queries [tb, tb + kTokPerGroup) of
-// sequence sq (the whole batch when not causal) against columns [kb, ke)
+// sequence sl (the whole batch when not causal) against columns [kb, ke)
 // (ke clamped to the row width); first_split: the unit holding column 0
 // writes row_len.  kbuf / ks_lds: the work-group's LDS key chunks.  Every
 // thread of the work-group calls it with the same arguments.
@@ -228,7 +256,7 @@ __device__ __forceinline__ void prefill_unit(
     KeyChunks &kbuf, KeyScales &ks_lds, const uint8_t *__restrict__ q,
     const float *__restrict__ q_scale, const uint8_t *__restrict__ k,
     const float *__restrict__ k_scale, int32_t T, int32_t H, int32_t N,
-    float *__restrict__ scores, int64_t ld, const RaggedBatch &rb, int sq, int tb, int kb,
+    float *__restrict__ scores, int64_t ld, const RaggedBatch &rb, const SeqSlice &sl, int tb, int kb,
     int64_t ke_in, bool first_split)
 {
     const int tid = threadIdx.x;
@@ -244,20 +272,13 @@ __device__ __forceinline__ void prefill_unit(
     int64_t row0 = 0, row_end = T;
     int32_t klen = N, width = N;
     if constexpr (kCausal) {
-        int64_t a0 = rb.q_start[sq], a1 = rb.q_start[sq + 1];
-        a0 = a0 < 0 ? 0 : (a0 > T ? T : a0);
-        a1 = a1 < a0 ? a0 : (a1 > T ? T : a1);
-        row0 = __builtin_amdgcn_readfirstlane((int32_t)a0);
-        row_end = __builtin_amdgcn_readfirstlane((int32_t)a1);
-        // Keys outside k[0, N) are never read: a sequence whose slice leaves
-        // the buffer is cut to the part inside it.
-        const int64_t k0 = rb.k_start[sq];
-        int64_t kl = rb.k_len[sq];
-        kl = (k0 < 0 || k0 > N) ? 0 : (kl > N - k0 ? N - k0 : (kl < 0 ? 0 : kl));
-        klen = __builtin_amdgcn_readfirstlane((int32_t)kl);
+        row0 = __builtin_amdgcn_readfirstlane(sl.row0);
+        row_end = row0 + __builtin_amdgcn_readfirstlane(sl.q_len);
+        klen = __builtin_amdgcn_readfirstlane(sl.klen);
         width = rb.width;
-        k += (k0 < 0 || k0 > N ? 0 : k0) * kDepth;
-        k_scale += (k0 < 0 || k0 > N ? 0 : k0);
+        const int64_t k0 = __builtin_amdgcn_readfirstlane(sl.k0);
+        k += k0 * kDepth;
+        k_scale += k0;
     }
     const int q_len = (int)(row_end - row0);
     if (tb >= q_len)
@@ -284,36 +305,6 @@ __device__ __forceinline__ void prefill_unit(
             rb.row_len[t + lane] = visible(iw + lane);
     }
     const int chunks = (kc - kb + kChunkKeys - 1) / kChunkKeys;
-
-    // Query rows as f16 A operands: head 32 ht + col, depth 16 st + 8 half
-    // .. +8 (zero past H, and for a token past T); kHT head tiles of 32.
-    u32x4 a[kHT][8];
-#pragma unroll
-    for (int ht = 0; ht < kHT; ++ht) {
-        const int h = kPack ? col % 4 : 32 * ht + col;
-        const int u = kPack ? 8 * ht + col / 4 : 0;
-        const bool ok = u < tok_rows && h < H;
-        const uint8_t *src = q + ((ok ? t + u : 0) * H + (ok ? h : 0)) * kDepth + 8 * half;
-#pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            uint2 b = make_uint2(0u, 0u);
-            if (ok)
-                b = *reinterpret_cast<const uint2 *>(src + 16 * st);
-            a[ht][st] = f16_of_8_bytes(b.x, b.y);
-        }
-    }
-    // Scales of the heads the lane's accumulators hold: element i of tile ht
-    // is head 32 ht + 8 (i / 4) + 4 half + i % 4 (packed: head i % 4 of
-    // token 8 ht + 2 (i / 4) + half).
-    float qs[kHT][16];
-#pragma unroll
-    for (int ht = 0; ht < kHT; ++ht)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int h = kPack ? i % 4 : 32 * ht + 8 * (i / 4) + 4 * half + i % 4;
-            const int u = kPack ? 8 * ht + 2 * (i / 4) + half : 0;
-            qs[ht][i] = (u < tok_rows && h < H) ? q_scale[(t + u) * H + h] : 0.0f;
-        }
 
     // Key conversion: thread -> key tid / 4 of the chunk, 32 depth bytes at
     // 32 (tid % 4): two 16-byte loads, then four pieces of four conversions
@@ -347,6 +338,50 @@ __device__ __forceinline__ void prefill_unit(
         if (j == 3)
             ks_lds[buf][ck] = r.ks;
     };
+
+    // Every load the unit starts with -- its query rows, their scales and
+    // the first two key chunks -- is issued before any of them is used, so
+    // the unit waits for memory once.
+    // Query rows as f16 A operands: head 32 ht + col, depth 16 st + 8 half
+    // .. +8 (zero past H, and for a token past T); kHT head tiles of 32.
+    // The rows and their scales are read through descriptors spanning the
+    // wave's tokens, so a lane outside them reads zero without a branch.
+    const int64_t row_q = tok_ok ? t : 0;
+    const __amdgpu_buffer_rsrc_t qr =
+        uniform_rsrc(q + row_q * H * kDepth, tok_ok ? (uint32_t)(tok_rows * H * kDepth) : 0u);
+    const __amdgpu_buffer_rsrc_t qsr = uniform_rsrc(q_scale + row_q * H, tok_ok ? (uint32_t)(tok_rows * H * 4) : 0u);
+    uint2 q_raw[kHT][8];
+#pragma unroll
+    for (int ht = 0; ht < kHT; ++ht) {
+        const int h = kPack ? col % 4 : 32 * ht + col;
+        const int u = kPack ? 8 * ht + col / 4 : 0;
+        const uint32_t off = (u < tok_rows && h < H) ? (uint32_t)((u * H + h) * kDepth + 8 * half) : kDropped;
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+            q_raw[ht][st] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(qr, off + 16 * st, 0, 0));
+    }
+    // Scales of the heads the lane's accumulators hold: element i of tile ht
+    // is head 32 ht + 8 (i / 4) + 4 half + i % 4 (packed: head i % 4 of
+    // token 8 ht + 2 (i / 4) + half).
+    float qs[kHT][16];
+#pragma unroll
+    for (int ht = 0; ht < kHT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int h = kPack ? i % 4 : 32 * ht + 8 * (i / 4) + 4 * half + i % 4;
+            const int u = kPack ? 8 * ht + 2 * (i / 4) + half : 0;
+            const uint32_t off = (u < tok_rows && h < H) ? (uint32_t)((u * H + h) * 4) : kDropped;
+            qs[ht][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qsr, off, 0, 0));
+        }
+    Raw r0, r1;
+    load_chunk(0, r0);
+    load_chunk(1, r1);
+    u32x4 a[kHT][8];
+#pragma unroll
+    for (int ht = 0; ht < kHT; ++ht)
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+            a[ht][st] = f16_of_8_bytes(q_raw[ht][st].x, q_raw[ht][st].y);
 
     // Scores of this wave's tokens for keys [kb, ke); a wave past T has no
     // records.  Packed, the descriptor spans the wave's rows (at most 2^30
@@ -501,15 +536,10 @@ __device__ __forceinline__ void prefill_unit(
     // c + 2 is converted into the third.  One barrier per chunk covers both
     // hazards: chunk c + 2 visible before chunk c + 1's last tile reads it,
     // and buffer c % 3 read out before chunk c + 3 is written into it.
-    {
-        Raw r0, r1;
-        load_chunk(0, r0);
-        load_chunk(1, r1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            store_piece(r0, 0, j);
-            store_piece(r1, 1, j);
-        }
+    for (int j = 0; j < 4; ++j) {
+        store_piece(r0, 0, j);
+        store_piece(r1, 1, j);
     }
     __syncthreads();
 
@@ -594,13 +624,30 @@ __device__ __forceinline__ void prefill_unit(
     }
     if constexpr (kCausal) {
         // The -inf tail past the computed chunks: columns [kb + 128 chunks, ke)
-        // of the wave's rows.
-        const int fill0 = chunks * kChunkKeys;
-        for (int u = 0; u < tok_rows; ++u)
-            for (int n = fill0 + lane; n < ke - kb; n += kWave)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), out,
-                                                      (uint32_t)(u * ld * 4) + (uint32_t)n * 4u, 0,
+        // of the wave's rows, 16 bytes per lane from the row's first 16-byte
+        // boundary on (single columns before it and after the last whole
+        // quad).
+        const int fill0 = chunks * kChunkKeys, fill1 = ke - kb;
+        const uint32_t ninf = __float_as_uint(-INFINITY);
+        const u32x4 ninf4 = {ninf, ninf, ninf, ninf};
+        for (int u = 0; u < tok_rows && fill0 < fill1; ++u) {
+            const uint32_t row = (uint32_t)(u * ld * 4);
+            const int mis = (int)(((uintptr_t)out_base / 4 + (uintptr_t)u * ld + fill0) & 3);
+            const int lead = (4 - mis) & 3;
+            const int head = lead < fill1 - fill0 ? lead : fill1 - fill0;
+            const int a0 = fill0 + head;
+            const int quads = (fill1 - a0) >> 2;
+            const int t0 = a0 + 4 * quads;
+            if (lane < head)
+                __builtin_amdgcn_raw_buffer_store_b32(ninf, out, row + (uint32_t)(fill0 + lane) * 4u, 0,
                                                       kStreamingStore);
+            for (int qd = lane; qd < quads; qd += kWave)
+                __builtin_amdgcn_raw_buffer_store_b128(ninf4, out, row + (uint32_t)(a0 + 4 * qd) * 4u, 0,
+                                                       kStreamingStore);
+            if (lane < fill1 - t0)
+                __builtin_amdgcn_raw_buffer_store_b32(ninf, out, row + (uint32_t)(t0 + lane) * 4u, 0,
+                                                      kStreamingStore);
+        }
     }
 }
 
@@ -615,111 +662,118 @@ __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_h64_kernel
     __shared__ KeyScales ks_lds;
     constexpr int kTokPerGroup = kH64Waves * (kPack ? 8 * kHT : 1);
     const int kb = blockIdx.y * keys_per_group;
+    const SeqSlice sl = kCausal ? seq_slice(rb, blockIdx.z, T, N) : SeqSlice{0, T, 0, N};
     prefill_unit<kHT, kPack, kCausal, kBlockMax>(kbuf, ks_lds, q, q_scale, k, k_scale, T, H, N, scores,
-                                                 ld, rb, blockIdx.z, blockIdx.x * kTokPerGroup, kb,
+                                                 ld, rb, sl, blockIdx.x * kTokPerGroup, kb,
                                                  (int64_t)kb + keys_per_group, blockIdx.y == 0);
 }
 
-// Chunks a causal query group computes: its last query's visible keys
-// (clamped as prefill_unit clamps them) in 128-key chunks.
-__device__ __forceinline__ int64_t group_chunks(int32_t q_len, int32_t klen, int32_t width, int x)
-{
-    const int last = (x + 1) * kH64Waves - 1 < q_len ? (x + 1) * kH64Waves - 1 : q_len - 1;
-    int64_t c = (int64_t)klen - q_len + last + 1;
-    const int64_t hi = klen < width ? klen : width;
-    c = c > hi ? hi : (c < 0 ? 0 : c);
-    return (c + kChunkKeys - 1) / kChunkKeys;
-}
-
-// The ragged causal batch with a balanced schedule (one token per wave):
-// the batch's work is the list of (sequence, group of eight queries, chunk
-// of 128 visible keys) in that order, and work-group b of G takes positions
-// [W b / G, W (b + 1) / G) of it, W its length -- a share equal to within
-// one chunk, whatever the sequences' lengths.  A share is a few segments of
-// consecutive chunks of one query group; each runs as a prefill_unit over
-// the segment's columns (the group's last segment also fills its rows with
-// -inf up to the width).  A group with no visible key is a zero-chunk
-// segment of the work-group whose share holds its list position (the last
-// work-group for one past the end).  Every thread walks the list
-// identically, so the work-group's barriers match.
+// The ragged causal batch with a balanced schedule (one token per wave; the
+// schedule itself is causal_share.hpp's): work-group b runs its share of the
+// batch's cost line as a few segments of consecutive chunks of one query
+// group, each a prefill_unit over the segment's columns (the group's last
+// segment also fills its rows with -inf up to the width).  The share is
+// found without walking the batch: each lane costs four sequences in closed
+// form, a wave scan and a ballot give the sequence holding the share's
+// start, and a binary search the group.  Every thread computes the same
+// walk, so the work-group's barriers match.
 template <int kHT>
 __global__ __launch_bounds__(kH64Waves * kWave, 2) void score_prefill_balanced_kernel(
     const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
     const uint8_t *__restrict__ k, const float *__restrict__ k_scale, int32_t T, int32_t H,
     int32_t N, int32_t num_seqs, float *__restrict__ scores, int64_t ld, RaggedBatch rb)
 {
+    static_assert(kCausalGroupRows == kH64Waves && kCausalChunkKeys == kChunkKeys,
+                  "the schedule's groups and chunks are the unit's");
     __shared__ __align__(16) KeyChunks kbuf;
     __shared__ KeyScales ks_lds;
     const int lane = threadIdx.x % kWave;
-    // Query and key counts of sequence s, clamped as prefill_unit clamps them.
-    auto seq_dims = [&](int s, int32_t &q_len, int32_t &klen) {
-        int64_t a0 = rb.q_start[s], a1 = rb.q_start[s + 1];
-        a0 = a0 < 0 ? 0 : (a0 > T ? T : a0);
-        a1 = a1 < a0 ? a0 : (a1 > T ? T : a1);
-        const int64_t k0 = rb.k_start[s];
-        int64_t kl = rb.k_len[s];
-        kl = (k0 < 0 || k0 > N) ? 0 : (kl > N - k0 ? N - k0 : (kl < 0 ? 0 : kl));
-        q_len = __builtin_amdgcn_readfirstlane((int32_t)(a1 - a0));
-        klen = __builtin_amdgcn_readfirstlane((int32_t)kl);
+    auto causal = [&](const SeqSlice &sl) {
+        return CausalSeq{sl.q_len, sl.klen, sl.klen < rb.width ? sl.klen : rb.width};
     };
-    // Chunks of sequence s: the lanes take its groups in turn and a wave sum
-    // joins them.
-    auto seq_chunks = [&](int32_t q_len, int32_t klen) {
-        const int groups = (q_len + kH64Waves - 1) / kH64Waves;
-        int64_t mine = 0;
-        for (int x = lane; x < groups; x += kWave)
-            mine += group_chunks(q_len, klen, rb.width, x);
+    auto uniform64 = [](int64_t v) {
+        return (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v));
+    };
+    const int64_t fill_units = causal_fill_units(rb.width);
+
+    // Lane l costs sequences 4 l .. 4 l + 3; an exclusive scan over the
+    // lanes places them on the cost line.  Every lane loads its four
+    // sequences' entries (a lane past the batch rereads the last one) before
+    // any is used, so the wave waits for memory once: the empty asm
+    // statements take the loaded values as they are, which keeps the
+    // compiler from moving a load behind a branch.
+    int32_t qa[4], qb[4], ka[4], kn[4];
 #pragma unroll
-        for (int d = 32; d >= 1; d >>= 1)
-            mine += __shfl_xor(mine, d);
-        return (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)mine) |
-               ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)(mine >> 32)) << 32);
-    };
-    int64_t W = 0;
-    for (int s = 0; s < num_seqs; ++s) {
-        int32_t q_len, klen;
-        seq_dims(s, q_len, klen);
-        W += seq_chunks(q_len, klen);
+    for (int i = 0; i < 4; ++i) {
+        const int s = 4 * lane + i < num_seqs ? 4 * lane + i : num_seqs - 1;
+        qa[i] = rb.q_start[s];
+        qb[i] = rb.q_start[s + 1];
+        ka[i] = rb.k_start[s];
+        kn[i] = rb.k_len[s];
     }
+    SeqSlice mine[4];
+    int64_t cost[4], lane_cost = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        asm volatile("" : "+v"(qa[i]), "+v"(qb[i]), "+v"(ka[i]), "+v"(kn[i]));
+        const SeqSlice sl = slice_of(qa[i], qb[i], ka[i], kn[i], T, N);
+        mine[i] = 4 * lane + i < num_seqs ? sl : SeqSlice{0, 0, 0, 0};
+        const CausalSeq c = causal(mine[i]);
+        cost[i] = causal_cost_before(c, causal_groups(c), fill_units);
+        lane_cost += cost[i];
+    }
+    int64_t excl = lane_cost;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int64_t y = __shfl_up(excl, d);
+        excl += lane >= d ? y : 0;
+    }
+    const int64_t total = uniform64(__shfl(excl, kWave - 1));
+    excl -= lane_cost;
     const int64_t G = gridDim.x, b = blockIdx.x;
-    const int64_t start = W * b / G, end = W * (b + 1) / G;
-    const bool last_block = b == G - 1;
-    // Walk the list to this share: whole sequences first, then groups.
-    int64_t pos = 0;
-    for (int s = 0; s < num_seqs && pos <= end; ++s) {
-        int32_t q_len, klen;
-        seq_dims(s, q_len, klen);
-        const int groups = (q_len + kH64Waves - 1) / kH64Waves;
-        if (groups == 0)
-            continue;
-        const int64_t tot = seq_chunks(q_len, klen);
-        // A sequence entirely before the share is skipped (one entirely
-        // after it ends the walk, by the loop condition); a sequence ending
-        // exactly at `start` may still hold zero-chunk groups at `start`.
-        if (pos + tot < start) {
-            pos += tot;
-            continue;
-        }
-        for (int x = 0; x < groups; ++x) {
-            const int64_t nc = group_chunks(q_len, klen, rb.width, x);
-            // This group's list positions [pos, pos + nc) inside [start, end),
-            // or a zero-chunk group at a position this share owns.
-            const int64_t a = pos > start ? pos : start;
-            const int64_t e = pos + nc < end ? pos + nc : end;
-            const bool owns_empty = nc == 0 && ((pos >= start && pos < end) || (last_block && pos >= W));
-            if (a < e || owns_empty) {
-                const int64_t ca = nc == 0 ? 0 : a - pos, cb = nc == 0 ? 0 : e - pos;
-                const int64_t ke = cb == nc ? (int64_t)rb.width : cb * kChunkKeys;
-                prefill_unit<kHT, false, true>(kbuf, ks_lds, q, q_scale, k, k_scale, T, H, N, scores,
-                                               ld, rb, s, x * kH64Waves, (int)(ca * kChunkKeys), ke,
-                                               ca == 0);
-                __syncthreads();   // the next unit rewrites the LDS chunks
+    const int64_t lo = total * b / G, hi = total * (b + 1) / G;
+    if (lo >= hi)
+        return;
+    // The sequence holding cost lo (lo < total: exactly one lane has it).
+    int found = -1;
+    int64_t found_base = 0;
+    SeqSlice found_sl{0, 0, 0, 0};
+    {
+        int64_t base = excl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (cost[i] > 0 && base <= lo && lo < base + cost[i]) {
+                found = 4 * lane + i;
+                found_base = base;
+                found_sl = mine[i];
             }
-            pos += nc;
-            if (pos > end || (pos == end && !last_block && nc > 0))
-                break;
+            base += cost[i];
         }
     }
+    const int src = (int)__builtin_ctzll(__ballot(found >= 0));
+    const int s = __builtin_amdgcn_readlane(found, src);
+    const int64_t base =
+        (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)((uint64_t)found_base >> 32), src) << 32) |
+                  (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)found_base, src));
+    SeqSlice sl{__builtin_amdgcn_readlane(found_sl.row0, src), __builtin_amdgcn_readlane(found_sl.q_len, src),
+                __builtin_amdgcn_readlane(found_sl.k0, src), __builtin_amdgcn_readlane(found_sl.klen, src)};
+    const CausalSeq c = causal(sl);
+    auto next = [&](int t) {
+        sl = seq_slice(rb, t, T, N);
+        sl.row0 = __builtin_amdgcn_readfirstlane(sl.row0);
+        sl.q_len = __builtin_amdgcn_readfirstlane(sl.q_len);
+        sl.k0 = __builtin_amdgcn_readfirstlane(sl.k0);
+        sl.klen = __builtin_amdgcn_readfirstlane(sl.klen);
+        return causal(sl);
+    };
+    auto unit = [&](int64_t x, int64_t ja, int64_t ke, bool first) {
+        prefill_unit<kHT, false, true>(kbuf, ks_lds, q, q_scale, k, k_scale, T, H, N, scores, ld, rb, sl,
+                                       (int)(x * kH64Waves), (int)(ja * kChunkKeys), ke, first);
+        __syncthreads();   // the next unit rewrites the LDS chunks
+    };
+    causal_share_walk(lo, hi, s, num_seqs, base, c, causal_group_at(c, base, lo, fill_units), fill_units,
+                      rb.width, next, unit);
 }
 
 // ---------------------------------------------------------------------------
