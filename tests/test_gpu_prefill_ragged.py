@@ -139,3 +139,37 @@ def test_most_sequences_in_one_call():
     assert np.array_equal(row_len, want_len)
     assert_scores_close(got, want, "65,535 sequences")
     assert np.array_equal(ids, oracle.topk16(got, valid_len=want_len))
+
+
+@pytest.mark.parametrize("H", [20, 64])
+def test_most_sequences_of_the_balanced_schedule(H):
+    """256 sequences, the most the balanced schedule takes (every lane costs
+    four of them): empty sequences, query groups past their few keys
+    (zero-chunk groups owned by whichever share holds them), one-chunk and
+    several-chunk groups, so that shares start and end inside sequences,
+    at group ends and on empty groups.  The oracle scores each sequence on
+    its own (the pieces run on host threads)."""
+    rng = np.random.default_rng(256 + H)
+    S = 256
+    q_lens = rng.integers(0, 21, S)
+    q_lens[rng.integers(0, S, 40)] = 0
+    k_lens = rng.integers(0, 300, S)
+    k_lens[::17] = rng.integers(0, 6, len(k_lens[::17]))
+    p, q_start, k_start, k_len = ragged_batch(77 + H, list(q_lens), list(k_lens), H, gap=1)
+    width = 310
+    announce(f"ragged prefill 256 sequences H={H}")
+    got, row_len, ids = run(p, q_start, k_start, k_len, width, width + 2)
+
+    def one(s):
+        a0, a1, k0, kl = int(q_start[s]), int(q_start[s + 1]), int(k_start[s]), int(k_len[s])
+        return oracle.score_prefill_ragged(p.q[a0:a1], p.q_scale[a0:a1], p.k[k0:k0 + kl],
+                                           p.k_scale[k0:k0 + kl], np.array([0, a1 - a0], np.int32),
+                                           np.zeros(1, np.int32), np.array([kl], np.int32), width)
+
+    parts = oracle_pool.map_pieces(one, range(S), "ragged sequences")
+    want = np.concatenate([w for w, _ in parts])
+    want_len = np.concatenate([n for _, n in parts])
+    assert np.array_equal(row_len, want_len), "row_len differs"
+    assert_scores_close(got[:, :width], want, f"256 sequences H={H}")
+    assert (got[:, width:].view(np.int32) == CANARY_F32.view(np.int32)).all(), "write past width"
+    assert np.array_equal(ids, oracle.topk16(got[:, :width], valid_len=want_len)), "top-16 differs"
