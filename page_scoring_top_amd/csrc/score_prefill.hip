@@ -25,7 +25,7 @@
 // of indexer_score_prefill_ragged, either one unit per work-group of a grid
 // or, for up to 256 sequences with one token per wave, as a balanced
 // schedule: one work-group per compute unit, each taking an equal share of
-// the batch's chunks.  It also runs the first pass of the fused top-16
+// the batch's estimated cost (causal_share.hpp).  It also runs the first pass of the fused top-16
 // (indexer_prefill_topk16), keeping per-block records instead of storing
 // scores; the second pass, prefill_topk_rescore_kernel, selects from them
 // (see the section near the end).  More heads take the general kernel: a
@@ -229,7 +229,7 @@ constexpr int kBlockKeys = kBlockTiles * kKeysPerTile;        // 1,024
 // tile ht is then head i % 4 of token 8 ht + 2 (i / 4) + half, so the head
 // sum of a (token, key) score is four elements of one lane, and a lane
 // stores 4 kHT scores per tile.
-// kCausal: a ragged batch of sequences (sq), each query row masked
+// kCausal: a ragged batch of sequences (sl), each query row masked
 // causally and its row filled with -inf past its visible keys.  Sequence s
 // owns query rows [q_start[s], q_start[s+1]) and keys k_start[s] ..
 // + k_len[s]; its queries are the last q_len tokens of its context, so
@@ -1121,7 +1121,7 @@ namespace {
 // 128 keys (at most 2^20 per work-group) so the grid holds about one
 // work-group per compute unit.
 // Sequences up to which a causal launch of the one-token path takes the
-// balanced schedule (each work-group walks the whole sequence list once).
+// balanced schedule (each lane of a work-group's waves costs four of them).
 constexpr int32_t kBalancedMaxSeqs = 256;
 // Work-groups a causal launch of the one-token path aims at (about four
 // per compute unit) when it takes the grid instead.
