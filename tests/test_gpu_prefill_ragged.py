@@ -76,12 +76,14 @@ def test_ragged_batch(H, case):
     assert np.array_equal(ids, want_ids), "top-16 differs"
 
 
-def test_width_below_context():
+@pytest.mark.parametrize("H", [4, 20])
+def test_width_below_context(H):
     """Rows are cut at the width: counts clamp to it and nothing is written
-    past it."""
-    p, q_start, k_start, k_len = ragged_batch(7, [40, 8], [900, 50], 4)
+    past it (four heads: the packed grid; 20: the balanced schedule, whose
+    costs clamp to the width too)."""
+    p, q_start, k_start, k_len = ragged_batch(7, [40, 8], [900, 50], H)
     width = 300
-    announce("ragged prefill width below context")
+    announce(f"ragged prefill width below context H={H}")
     got, row_len, _ = run(p, q_start, k_start, k_len, width, width + 1)
     want, want_len = oracle.score_prefill_ragged(p.q, p.q_scale, p.k, p.k_scale, q_start, k_start,
                                                  k_len, width)
@@ -141,7 +143,7 @@ def test_most_sequences_in_one_call():
     assert np.array_equal(ids, oracle.topk16(got, valid_len=want_len))
 
 
-@pytest.mark.parametrize("H", [20, 64])
+@pytest.mark.parametrize("H", [20, 33, 64])
 def test_most_sequences_of_the_balanced_schedule(H):
     """256 sequences, the most the balanced schedule takes (every lane costs
     four of them): empty sequences, query groups past their few keys
